@@ -1,0 +1,221 @@
+/*
+ * sdpa.h - C ABI of the MI355X (gfx950) fused scaled-dot-product attention library.
+ *
+ * The library computes, on one GPU:
+ *   forward   O = softmax(scale * Q K^T + mask) V, and the per-row log-sum-exp
+ *             LSE_i = log sum_j exp(scale * q_i . k_j) over the visible keys
+ *             (natural log, scores include the scale);
+ *   backward  dQ, dK, dV of a loss through O and LSE, recomputing P from LSE;
+ *   merge     the LSE merge of two partial results over disjoint (or not) key sets,
+ *             forward and backward.
+ * Sources: "[PyTorch] fused CUDNN attention kernel not properly handling strides"
+ * (TransformerEngine issue 1195: q/k/v as strided views of a packed tensor, qkv_format,
+ * window_size, softmax_scale, GQA groups), "Add support for cuDNN FusedAttention + THD +
+ * CP" (TransformerEngine issue 885: THD with cu_seqlens), "Significant Accuracy
+ * Difference between Compiled and Eager Flex Attention" (PyTorch issue 135161:
+ * return_lse, the merge_attn helper, the sliding-window masks, true fp32).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are described by a base pointer and per-dimension strides counted in
+ *   ELEMENTS, given in the logical order of the descriptor's layout:
+ *     BSHD (b, s, h, d)   SBHD (s, b, h, d)   BHSD (b, h, s, d)   THD (t, h, d)
+ *   The last (d) stride must be 1.  No other stride is assumed: q, k and v may be views
+ *   of one packed [s, b, hq + 2 hk, d] buffer (base pointers offset by whole heads,
+ *   strides (hq+2hk)*d, ..., d, 1).  Packed layouts are not separate tags: pass the three
+ *   views.  Nothing is ever made contiguous or copied behind the caller's back.
+ * - Row statistics (LSE, dLSE) are fp32 [b, h, s] for BSHD/SBHD/BHSD and [h, t] for THD,
+ *   again with element strides in that order (stride[2] unused for THD).
+ * - Input strides may be 0 (broadcast) or overlap (q/k/v from one buffer).  Outputs must
+ *   not map two elements to one address, must not overlap each other and must not overlap
+ *   any input.  Outputs that are disjoint head ranges of one packed buffer are accepted.
+ * - Every call validates completely before launching; on any error it returns a non-zero
+ *   status, writes nothing and leaves a message for sdpa_last_error().
+ * - Compute calls are asynchronous on the given HIP stream (a hipStream_t; NULL = the
+ *   default stream).  They never synchronise the device.  All buffers, the workspace
+ *   included, belong to the caller and must stay alive until the stream reaches the work.
+ *   The library allocates no device memory and holds no mutable global state apart from
+ *   the per-thread last-error message.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDPA_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL = 1,        /* a required pointer is NULL                                */
+  SDPA_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or too large */
+  SDPA_ERR_STRIDE = 3,      /* d-stride != 1, negative stride, or an output self-overlaps */
+  SDPA_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size              */
+  SDPA_ERR_ALIAS = 5,       /* outputs overlap each other or an input                    */
+  SDPA_ERR_UNSUPPORTED = 6, /* dtype / head_dim / layout combination not built           */
+  SDPA_ERR_WORKSPACE = 7,   /* workspace missing or too small                            */
+  SDPA_ERR_HIP = 8,         /* a HIP launch failed; the HIP message is in last_error     */
+  SDPA_ERR_ARG = 9          /* an enum or option is out of range                         */
+};
+
+enum sdpa_layout { SDPA_LAYOUT_BSHD = 0, SDPA_LAYOUT_SBHD = 1, SDPA_LAYOUT_BHSD = 2, SDPA_LAYOUT_THD = 3 };
+enum sdpa_dtype { SDPA_DTYPE_F16 = 0, SDPA_DTYPE_BF16 = 1, SDPA_DTYPE_F32 = 2 };
+/* Where the diagonal of a window sits when seqlen_q != seqlen_k: query i is aligned with
+ * key i (TOP_LEFT) or with key i + seqlen_k - seqlen_q (BOTTOM_RIGHT).  Per sequence for THD. */
+enum sdpa_diag_align { SDPA_ALIGN_TOP_LEFT = 0, SDPA_ALIGN_BOTTOM_RIGHT = 1 };
+
+/* A q/k/v/o/dO/dq/dk/dv tensor: element (i0,i1,i2,i3) of the layout's logical order lives at
+ * data + sum(i_n * stride[n]) elements.  For THD only stride[0..2] are read. */
+typedef struct sdpa_tensor {
+  void* data;
+  int64_t stride[4];
+} sdpa_tensor_t;
+
+/* An fp32 row statistic (LSE or dLSE): [b,h,s] or, for THD, [h,t]. */
+typedef struct sdpa_rowstat {
+  float* data;
+  int64_t stride[3];
+} sdpa_rowstat_t;
+
+/* Problem description shared by q, k, v, o, dO, dq, dk, dv of one call.
+ *
+ * batch       number of sequences (THD: entries of cu_seqlens minus one).
+ * seqlen_q/k  sequence lengths (THD: the maxima over the batch; rows beyond a sequence's
+ *             own length are never touched).
+ * heads_q/kv  query and key/value heads; heads_q must be a multiple of heads_kv (GQA/MQA):
+ *             q head h reads kv head h / (heads_q / heads_kv).
+ * head_dim    D, shared by q, k, v; 32, 64 or 128.
+ * cu_seqlens_q/k  THD only: DEVICE int32[batch+1], non-decreasing, starting at 0; may be the
+ *             same pointer.  Entries are clamped to [0, total] on the device so a bad array
+ *             cannot cause out-of-bounds access (it gives wrong rows instead).
+ * total_q/k   THD only: number of packed rows of q and of k/v (= cu_seqlens[batch]).
+ * softmax_scale  multiplies Q K^T; required, no default.
+ * window_left/right  key j is visible to query i iff
+ *             (window_left == -1 or j >= i + off - window_left) and
+ *             (window_right == -1 or j <= i + off + window_right),
+ *             off = 0 (TOP_LEFT) or seqlen_k - seqlen_q (BOTTOM_RIGHT).  -1 is unbounded,
+ *             (-1,-1) no mask, (-1,0) causal, (128,0) a 129-key causal band.  Any other
+ *             value, negative ones included, is an offset bound: (-1,-129) keeps only keys
+ *             at least 129 behind the query.  A query with no visible key gets O = 0 and
+ *             LSE = -inf and contributes no gradient.
+ * diag_align  enum sdpa_diag_align. */
+typedef struct sdpa_desc {
+  int32_t layout;
+  int32_t dtype;
+  int32_t batch;
+  int32_t seqlen_q;
+  int32_t seqlen_k;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int64_t total_q;
+  int64_t total_k;
+  float softmax_scale;
+  int32_t window_left;
+  int32_t window_right;
+  int32_t diag_align;
+} sdpa_desc_t;
+
+/* Merge description: rows of x are [layout order] tensors of `heads` heads of head_dim,
+ * lse is the matching row statistic.  THD uses `total` rows and ignores batch/seqlen. */
+typedef struct sdpa_merge_desc {
+  int32_t layout;
+  int32_t dtype;
+  int32_t batch;
+  int32_t seqlen;
+  int32_t heads;
+  int32_t head_dim;
+  int64_t total;
+} sdpa_merge_desc_t;
+
+/* Library version (SDPA_VERSION of the build). */
+int sdpa_version(void);
+
+/* Message for the last failing call on this host thread ("" if none).  The string is
+ * owned by the library and valid until the next call on the same thread. */
+const char* sdpa_last_error(void);
+
+/* Forward workspace size in bytes for `desc` (0 unless layout is THD, where it holds the
+ * longest-first work list built from cu_seqlens).  Host only. */
+int sdpa_fwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes);
+
+/* Host-only dry run of sdpa_fwd's validation: same arguments, no launch, no device access. */
+int sdpa_fwd_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                      const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                      size_t workspace_bytes);
+
+/* Forward (fused, online softmax; TransformerEngine issue 1195 repro calls, PyTorch issue
+ * 135161 return_lse=True).  Reads q, k, v; writes o (same dtype and logical shape as q) and
+ * lse (fp32).  `lse->data` may be NULL to skip writing LSE. */
+int sdpa_fwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+             const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward workspace size in bytes: fp32 Delta_i = dO_i . O_i - dLSE_i for every q row,
+ * plus the THD work lists.  Host only. */
+int sdpa_bwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes);
+
+/* Host-only dry run of sdpa_bwd's validation. */
+int sdpa_bwd_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                      const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                      const sdpa_tensor_t* dout, const sdpa_rowstat_t* dlse,
+                      const sdpa_tensor_t* dq, const sdpa_tensor_t* dk, const sdpa_tensor_t* dv,
+                      size_t workspace_bytes);
+
+/* Backward from the saved LSE (PyTorch issue 135161: gradients through O and through the
+ * returned LSE).  Reads q, k, v, o, lse (from sdpa_fwd), dout and optionally dlse
+ * (dlse == NULL or dlse->data == NULL means dL/dLSE = 0).  Writes dq (q's shape), dk and dv
+ * (k's shape; summed over the q heads of each group).  No atomics: every output element
+ * has one writer.  accumulate = 0 overwrites, 1 adds to the existing contents (to sum the
+ * gradients of several partial attentions into one buffer). */
+int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+             const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+             const sdpa_tensor_t* dout, const sdpa_rowstat_t* dlse, const sdpa_tensor_t* dq,
+             const sdpa_tensor_t* dk, const sdpa_tensor_t* dv, int accumulate, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* Host-only dry runs of the merge calls. */
+int sdpa_merge_fwd_validate(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* x_a,
+                            const sdpa_rowstat_t* lse_a, const sdpa_tensor_t* x_b,
+                            const sdpa_rowstat_t* lse_b, const sdpa_tensor_t* x,
+                            const sdpa_rowstat_t* lse);
+int sdpa_merge_bwd_validate(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* x_a,
+                            const sdpa_rowstat_t* lse_a, const sdpa_tensor_t* x_b,
+                            const sdpa_rowstat_t* lse_b, const sdpa_tensor_t* g,
+                            const sdpa_rowstat_t* g_lse, const sdpa_tensor_t* dx_a,
+                            const sdpa_rowstat_t* dlse_a, const sdpa_tensor_t* dx_b,
+                            const sdpa_rowstat_t* dlse_b);
+
+/* LSE merge of two partials (PyTorch issue 135161, merge_attn): per row,
+ * m = max(lse_a, lse_b), w = exp(lse - m), x = (x_a w_a + x_b w_b) / (w_a + w_b),
+ * lse = m + log(w_a + w_b); two -inf rows give (0, -inf).  Computed in fp32, x rounded to
+ * the dtype.  `lse->data` may be NULL to skip it. */
+int sdpa_merge_fwd(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* x_a,
+                   const sdpa_rowstat_t* lse_a, const sdpa_tensor_t* x_b,
+                   const sdpa_rowstat_t* lse_b, const sdpa_tensor_t* x,
+                   const sdpa_rowstat_t* lse, void* stream);
+
+/* Backward of the merge for upstream g = dL/dx and g_lse = dL/dlse (NULL = 0), with
+ * alpha = w_a / (w_a + w_b), beta = w_b / (w_a + w_b):
+ *   dx_a = alpha g,  dx_b = beta g,
+ *   dlse_a = alpha beta sum_d g (x_a - x_b) + alpha g_lse,  dlse_b symmetric.
+ * Recomputes alpha and beta from lse_a and lse_b (no saved output needed). */
+int sdpa_merge_bwd(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* x_a,
+                   const sdpa_rowstat_t* lse_a, const sdpa_tensor_t* x_b,
+                   const sdpa_rowstat_t* lse_b, const sdpa_tensor_t* g,
+                   const sdpa_rowstat_t* g_lse, const sdpa_tensor_t* dx_a,
+                   const sdpa_rowstat_t* dlse_a, const sdpa_tensor_t* dx_b,
+                   const sdpa_rowstat_t* dlse_b, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

@@ -1,0 +1,742 @@
+// Fused attention backward for gfx950, recomputing P from the saved LSE.
+//
+// Gradient of a loss through O and through the returned LSE (PyTorch issue 135161,
+// "Significant Accuracy Difference between Compiled and Eager Flex Attention": the merged
+// LSE is differentiated, so the backward receives dLSE):
+//   Delta_i = dO_i . O_i - dLSE_i,   P_ij = exp(s_ij - LSE_i),   dP = dO V^T,
+//   dS_ij = P_ij (dP_ij - Delta_i),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// Three launches on one stream, no atomics anywhere:
+//   pre   Delta for every query row (streaming, HBM bound);
+//   dq    one workgroup per 128 query rows of a q head, streaming the key tiles;
+//   dkdv  one workgroup per 128 keys of a kv head, streaming the query tiles of every q
+//         head of its group, so dK and dV of a GQA group are summed in registers.
+// In 16-bit mode the operands that must be contracted over rows (K in dq; Q and dO in
+// dkdv) are also kept transposed in LDS, written once per tile from the same registers
+// that fill the row-major copy.  fp32 mode uses true fp32 MFMA and reads the transposed
+// operand element-wise from the row-major tile.
+#include "device.h"
+#include "launch.h"
+#include "profile.h"
+
+namespace sdpa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int64_t delta_index(const Shape& s, int b, int h, const Seq& g, int i) {
+  return s.thd ? int64_t(h) * s.total_q + g.qrow0 + i : (int64_t(b) * s.hq + h) * s.sq + i;
+}
+
+// ----------------------------------------------------------------------------------------
+// pre-pass: Delta_i = dO_i . O_i - dLSE_i
+// ----------------------------------------------------------------------------------------
+template <int ES, bool BF, int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
+  constexpr int VPT = 16 / ES, TPR = D / VPT, RPB = kThreads / TPR;
+  const Shape& s = p.s;
+  const int tid = threadIdx.x;
+  const int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
+  const int64_t r = int64_t(blockIdx.x) * RPB + tid / TPR;
+  const bool live = r < rows;
+  int64_t b = 0, h, t;
+  if (s.thd) {
+    h = live ? r / s.total_q : 0;
+    t = live ? r % s.total_q : 0;
+  } else {
+    t = live ? r % s.sq : 0;
+    int64_t bh = live ? r / s.sq : 0;
+    h = bh % s.hq;
+    b = bh / s.hq;
+  }
+  const int c = (tid % TPR) * VPT;
+  float dot = 0.f;
+  if (live) {
+    const char* orow = static_cast<const char*>(p.o.ptr) + (b * p.o.sb + h * p.o.sh + t * p.o.ss + c) * ES;
+    const char* grow = static_cast<const char*>(p.dout.ptr) +
+                       (b * p.dout.sb + h * p.dout.sh + t * p.dout.ss + c) * ES;
+    uint4 ov = load16<ES>(orow, p.aligned & kAlO);
+    uint4 gv = load16<ES>(grow, p.aligned & kAlDO);
+    if constexpr (ES == 4) {
+      dot = __uint_as_float(ov.x) * __uint_as_float(gv.x) + __uint_as_float(ov.y) * __uint_as_float(gv.y) +
+            __uint_as_float(ov.z) * __uint_as_float(gv.z) + __uint_as_float(ov.w) * __uint_as_float(gv.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dot += to_f32<BF>(uint16_t(elem16(ov, e))) * to_f32<BF>(uint16_t(elem16(gv, e)));
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+  if (live && c == 0) {
+    float dl = p.dlse.ptr ? p.dlse.ptr[b * p.dlse.sb + h * p.dlse.sh + t * p.dlse.ss] : 0.f;
+    p.delta[r] = dot - dl;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// work decode shared by dq (query tiles, heaviest last tile first) and dkdv (key tiles)
+// ----------------------------------------------------------------------------------------
+struct BwdPos {
+  int b, h, tile;
+};
+
+__device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
+                                           const int32_t* count, int heads, int len, int tile_rows,
+                                           bool reverse, BwdPos& w) {
+  if (s.thd) {
+    int item = blockIdx.x / heads;
+    w.h = blockIdx.x % heads;
+    if (item >= *count) return false;
+    WorkItem it = work[item];
+    w.b = it.seq;
+    w.tile = it.tile;
+    return true;
+  }
+  int bh = s.batch * heads;
+  int nt = (len + tile_rows - 1) / tile_rows;
+  int t = blockIdx.x / bh;
+  int r = blockIdx.x % bh;
+  w.b = r / heads;
+  w.h = r % heads;
+  w.tile = reverse ? nt - 1 - t : t;
+  return true;
+}
+
+// Load a [64 rows x D] 16-bit tile into registers so that this thread holds RPT
+// consecutive rows of one 8-element column chunk (the layout both LDS copies need).
+template <int D>
+struct Tile16 {
+  static constexpr int ROWS = 64;
+  static constexpr int RPT = ROWS * D / 8 / kThreads;  // rows per thread
+  static constexpr int RP = D + 8;                     // row-major pitch (elements)
+  static constexpr int TP = ROWS + 8;                  // transposed pitch (elements)
+  static_assert(RPT >= 1 && RPT <= 4, "tile split");
+  uint4 r[RPT];
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t ss, int row0, int nrows, bool al) {
+    const int dc = threadIdx.x % (D / 8), rg = threadIdx.x / (D / 8);
+#pragma unroll
+    for (int x = 0; x < RPT; ++x) {
+      int row = row0 + rg * RPT + x;
+      r[x] = row < nrows ? load16<2>(base + row * ss + dc * 8, al) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store_rows(uint16_t* lds) const {
+    const int dc = threadIdx.x % (D / 8), rg = threadIdx.x / (D / 8);
+#pragma unroll
+    for (int x = 0; x < RPT; ++x)
+      *reinterpret_cast<uint4*>(&lds[(rg * RPT + x) * RP + dc * 8]) = r[x];
+  }
+  __device__ __forceinline__ void store_transposed(uint16_t* lds) const {
+    const int dc = threadIdx.x % (D / 8), rg = threadIdx.x / (D / 8);
+    const int pos = tpos(rg * RPT);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t* dst = &lds[(dc * 8 + e) * TP + pos];
+      if constexpr (RPT == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(elem16(r[0], e) | (elem16(r[1], e) << 16),
+                                                    elem16(r[2], e) | (elem16(r[3], e) << 16));
+      } else if constexpr (RPT == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = elem16(r[0], e) | (elem16(r[1], e) << 16);
+      } else {
+        *dst = uint16_t(elem16(r[0], e));
+      }
+    }
+  }
+};
+
+// Write 4 consecutive d values (scaled) of one row, adding to the old ones if asked.
+template <bool BF>
+__device__ __forceinline__ void out4_16(uint16_t* p, const float* v, float scale, bool al, bool acc) {
+  float x[4] = {v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale};
+  if (acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] += to_f32<BF>(p[i]);
+  }
+  store8(p, pack2<BF>(x[0], x[1]), pack2<BF>(x[2], x[3]), al);
+}
+
+__device__ __forceinline__ void out4_32(float* p, const float* v, float scale, bool al, bool acc) {
+  float x[4] = {v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale};
+  if (acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] += p[i];
+  }
+  store16<4>(p, make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                           __float_as_uint(x[3])), al);
+}
+
+// ----------------------------------------------------------------------------------------
+// dQ, 16-bit
+// ----------------------------------------------------------------------------------------
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq16_kernel(BwdParams p) {
+  constexpr int BM = kBwdQ, BN = kBwdQInner;
+  using T = Tile16<D>;
+  static_assert(BN == T::ROWS, "inner tile");
+  constexpr int NC = D / 16, NKB = BN / 32, NDB = D / 32, NPC = BN / 16;
+  __shared__ __align__(16) uint16_t sk_[BN * T::RP];
+  __shared__ __align__(16) uint16_t skt_[D * T::TP];
+  __shared__ __align__(16) uint16_t sv_[BN * T::RP];
+
+  const Shape& s = p.s;
+  BwdPos w;
+  if (!bwd_decode(s, p.work_q, p.count_q, s.hq, s.sq, BM, true, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int hk = w.h / s.group;
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh + g.qrow0 * p.q.ss;
+  const uint16_t* gb = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + w.h * p.dout.sh +
+                       g.qrow0 * p.dout.ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint16_t* dqb = static_cast<uint16_t*>(p.dq.ptr) + w.b * p.dq.sb + w.h * p.dq.sh + g.qrow0 * p.dq.ss;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN, kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  const int qw0 = q0 + wave * 32, qw1 = min(qw0 + 32, g.sq);
+  const int qi = qw0 + l32;
+  const bool qvalid = qi < g.sq;
+  int wj0 = 0, wj1 = 0;
+  if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+
+  uint4 qf[NC], gf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = qvalid ? load16<2>(qb + qi * p.q.ss + 16 * c + 8 * hf, p.aligned & kAlQ) : make_uint4(0, 0, 0, 0);
+    gf[c] = qvalid ? load16<2>(gb + qi * p.dout.ss + 16 * c + 8 * hf, p.aligned & kAlDO) : make_uint4(0, 0, 0, 0);
+  }
+  float lse2 = __builtin_inff(), dl = 0.f;
+  if (qvalid) {
+    float l = p.lse.ptr[w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss];
+    lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    dl = p.delta[delta_index(s, w.b, w.h, g, qi)];
+  }
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  T kt, vt;
+  for (int t = kt0; t < kt1; ++t) {
+    const int kbase = t * BN;
+    kt.load(kb, p.k.ss, kbase, g.sk, p.aligned & kAlK);
+    vt.load(vb, p.v.ss, kbase, g.sk, p.aligned & kAlV);
+    __syncthreads();  // previous tile fully consumed
+    kt.store_rows(sk_);
+    kt.store_transposed(skt_);
+    vt.store_rows(sv_);
+    __syncthreads();
+    if (kbase < wj1 && kbase + BN > wj0) {
+      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
+      uint4 dsf[NPC];
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2) {
+        f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          uint4 a = *reinterpret_cast<const uint4*>(&sk_[(k2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
+          st = mfma16<BF>(a, qf[c], st);
+          uint4 bv = *reinterpret_cast<const uint4*>(&sv_[(k2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
+          dp = mfma16<BF>(bv, gf[c], dp);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(st[r] * s.scale_log2 - lse2);
+          if (!full) {
+            int j = kbase + k2 * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (!visible(s, g, qi, j)) pr = 0.f;
+          }
+          ds[r] = pr * (dp[r] - dl);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          dsf[2 * k2 + h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                                        pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int c = 0; c < NPC; ++c) {
+          uint4 a = *reinterpret_cast<const uint4*>(&skt_[(db * 32 + l32) * T::TP + 16 * c + 8 * hf]);
+          acc[db] = mfma16<BF>(a, dsf[c], acc[db]);
+        }
+      }
+    }
+  }
+  if (qvalid) {
+    uint16_t* row = dqb + qi * p.dq.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float v[4] = {acc[db][4 * gq], acc[db][4 * gq + 1], acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+        out4_16<BF>(row + db * 32 + 8 * gq + 4 * hf, v, s.scale, p.aligned & kAlDQ, p.accumulate);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// dK, dV, 16-bit
+// ----------------------------------------------------------------------------------------
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv16_kernel(BwdParams p) {
+  constexpr int BK = kBwdK, BQ = kBwdKInner;
+  using T = Tile16<D>;
+  static_assert(BQ == T::ROWS, "inner tile");
+  constexpr int NC = D / 16, NQB = BQ / 32, NDB = D / 32, NQC = BQ / 16;
+  __shared__ __align__(16) uint16_t sq_[BQ * T::RP];
+  __shared__ __align__(16) uint16_t sqt_[D * T::TP];
+  __shared__ __align__(16) uint16_t sg_[BQ * T::RP];
+  __shared__ __align__(16) uint16_t sgt_[D * T::TP];
+  __shared__ __align__(16) float slse_[BQ];
+  __shared__ __align__(16) float sdl_[BQ];
+
+  const Shape& s = p.s;
+  BwdPos w;
+  if (!bwd_decode(s, p.work_k, p.count_k, s.hk, s.sk, BK, false, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int k0 = w.tile * BK;
+  if (k0 >= g.sk) return;
+  const int kend = min(k0 + BK, g.sk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int hk = w.h;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint16_t* dkb = static_cast<uint16_t*>(p.dk.ptr) + w.b * p.dk.sb + hk * p.dk.sh + g.krow0 * p.dk.ss;
+  uint16_t* dvb = static_cast<uint16_t*>(p.dv.ptr) + w.b * p.dv.sb + hk * p.dv.sh + g.krow0 * p.dv.ss;
+
+  int i0, i1;
+  query_range(s, g, k0, kend, i0, i1);
+  const int qt0 = i0 / BQ, qt1 = i1 > i0 ? (i1 + BQ - 1) / BQ : qt0;
+  const int kw0 = k0 + wave * 32, kw1 = min(kw0 + 32, g.sk);
+  const int kj = kw0 + l32;
+  const bool kvalid = kj < g.sk;
+  int wi0 = 0, wi1 = 0;
+  if (kw0 < kw1) query_range(s, g, kw0, kw1, wi0, wi1);
+
+  uint4 kf[NC], vf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    kf[c] = kvalid ? load16<2>(kb + kj * p.k.ss + 16 * c + 8 * hf, p.aligned & kAlK) : make_uint4(0, 0, 0, 0);
+    vf[c] = kvalid ? load16<2>(vb + kj * p.v.ss + 16 * c + 8 * hf, p.aligned & kAlV) : make_uint4(0, 0, 0, 0);
+  }
+  f32x16_t adk[NDB], adv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    adk[i] = zero16();
+    adv[i] = zero16();
+  }
+
+  T qt, gt;
+  for (int gi = 0; gi < s.group; ++gi) {
+    const int h = hk * s.group + gi;
+    const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss;
+    const uint16_t* gb = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh +
+                         g.qrow0 * p.dout.ss;
+    for (int t = qt0; t < qt1; ++t) {
+      const int qbase = t * BQ;
+      qt.load(qb, p.q.ss, qbase, g.sq, p.aligned & kAlQ);
+      gt.load(gb, p.dout.ss, qbase, g.sq, p.aligned & kAlDO);
+      float lv = __builtin_inff(), dv = 0.f;
+      if (tid < BQ) {
+        int i = qbase + tid;
+        if (i < g.sq) {
+          float l = p.lse.ptr[w.b * p.lse.sb + h * p.lse.sh + (g.qrow0 + i) * p.lse.ss];
+          lv = l == kNegInf ? __builtin_inff() : l * kLog2e;
+          dv = p.delta[delta_index(s, w.b, h, g, i)];
+        }
+      }
+      __syncthreads();
+      qt.store_rows(sq_);
+      qt.store_transposed(sqt_);
+      gt.store_rows(sg_);
+      gt.store_transposed(sgt_);
+      if (tid < BQ) {
+        slse_[tid] = lv;
+        sdl_[tid] = dv;
+      }
+      __syncthreads();
+      if (qbase < wi1 && qbase + BQ > wi0) {
+        const bool full = tile_full(s, g, qbase, min(qbase + BQ, g.sq), kw0, kw1);
+        uint4 pf[NQC], dsf[NQC];
+#pragma unroll
+        for (int qb2 = 0; qb2 < NQB; ++qb2) {
+          f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            uint4 a = *reinterpret_cast<const uint4*>(&sq_[(qb2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
+            st = mfma16<BF>(a, kf[c], st);
+            uint4 b2 = *reinterpret_cast<const uint4*>(&sg_[(qb2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
+            dp = mfma16<BF>(b2, vf[c], dp);
+          }
+          float pr[16], ds[16];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int ql = qb2 * 32 + 8 * g4 + 4 * hf;
+            float4 l4 = *reinterpret_cast<const float4*>(&slse_[ql]);
+            float4 d4 = *reinterpret_cast<const float4*>(&sdl_[ql]);
+            float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g4 + e;
+              float x = fast_exp2(st[r] * s.scale_log2 - la[e]);
+              if (!full && !visible(s, g, qbase + ql + e, kj)) x = 0.f;
+              pr[r] = x;
+              ds[r] = x * (dp[r] - da[e]);
+            }
+          }
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            pf[2 * qb2 + h2] = make_uint4(pack2<BF>(pr[8 * h2], pr[8 * h2 + 1]), pack2<BF>(pr[8 * h2 + 2], pr[8 * h2 + 3]),
+                                          pack2<BF>(pr[8 * h2 + 4], pr[8 * h2 + 5]), pack2<BF>(pr[8 * h2 + 6], pr[8 * h2 + 7]));
+            dsf[2 * qb2 + h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                                           pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int c = 0; c < NQC; ++c) {
+            uint4 a = *reinterpret_cast<const uint4*>(&sgt_[(db * 32 + l32) * T::TP + 16 * c + 8 * hf]);
+            adv[db] = mfma16<BF>(a, pf[c], adv[db]);
+            uint4 b2 = *reinterpret_cast<const uint4*>(&sqt_[(db * 32 + l32) * T::TP + 16 * c + 8 * hf]);
+            adk[db] = mfma16<BF>(b2, dsf[c], adk[db]);
+          }
+        }
+      }
+    }
+  }
+  if (kvalid) {
+    uint16_t* krow = dkb + kj * p.dk.ss;
+    uint16_t* vrow = dvb + kj * p.dv.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = db * 32 + 8 * gq + 4 * hf;
+        float a[4] = {adk[db][4 * gq], adk[db][4 * gq + 1], adk[db][4 * gq + 2], adk[db][4 * gq + 3]};
+        float b2[4] = {adv[db][4 * gq], adv[db][4 * gq + 1], adv[db][4 * gq + 2], adv[db][4 * gq + 3]};
+        out4_16<BF>(krow + d, a, s.scale, p.aligned & kAlDK, p.accumulate);
+        out4_16<BF>(vrow + d, b2, 1.f, p.aligned & kAlDV, p.accumulate);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// fp32: true fp32 MFMA 32x32x2, inner tiles of 32 rows, row-major LDS only
+// ----------------------------------------------------------------------------------------
+template <int D>
+struct Tile32 {
+  static constexpr int ROWS = 32;
+  static constexpr int RP = D + 4;
+  static constexpr int LDC = ROWS * D / 4 / kThreads;
+  static_assert(LDC >= 1, "tile split");
+  uint4 r[LDC];
+  __device__ __forceinline__ void load(const float* base, int64_t ss, int row0, int nrows, bool al) {
+#pragma unroll
+    for (int u = 0; u < LDC; ++u) {
+      int ci = threadIdx.x + u * kThreads;
+      int row = row0 + ci / (D / 4), col = (ci % (D / 4)) * 4;
+      r[u] = row < nrows ? load16<4>(base + row * ss + col, al) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(float* lds) const {
+#pragma unroll
+    for (int u = 0; u < LDC; ++u) {
+      int ci = threadIdx.x + u * kThreads;
+      *reinterpret_cast<uint4*>(&lds[(ci / (D / 4)) * RP + (ci % (D / 4)) * 4]) = r[u];
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
+  constexpr int BM = kBwdQ, BN = 32, H2 = D / 2, NDB = D / 32;
+  using T = Tile32<D>;
+  __shared__ __align__(16) float sk_[BN * T::RP];
+  __shared__ __align__(16) float sv_[BN * T::RP];
+
+  const Shape& s = p.s;
+  BwdPos w;
+  if (!bwd_decode(s, p.work_q, p.count_q, s.hq, s.sq, BM, true, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int hk = w.h / s.group;
+  const float* qb = static_cast<const float*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh + g.qrow0 * p.q.ss;
+  const float* gb = static_cast<const float*>(p.dout.ptr) + w.b * p.dout.sb + w.h * p.dout.sh + g.qrow0 * p.dout.ss;
+  const float* kb = static_cast<const float*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const float* vb = static_cast<const float*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  float* dqb = static_cast<float*>(p.dq.ptr) + w.b * p.dq.sb + w.h * p.dq.sh + g.qrow0 * p.dq.ss;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN, kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  const int qw0 = q0 + wave * 32, qw1 = min(qw0 + 32, g.sq);
+  const int qi = qw0 + l32;
+  const bool qvalid = qi < g.sq;
+  int wj0 = 0, wj1 = 0;
+  if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+
+  float qf[H2], gf[H2];
+#pragma unroll
+  for (int u = 0; u < H2 / 4; ++u) {
+    uint4 a = qvalid ? load16<4>(qb + qi * p.q.ss + hf * H2 + 4 * u, p.aligned & kAlQ) : make_uint4(0, 0, 0, 0);
+    uint4 b = qvalid ? load16<4>(gb + qi * p.dout.ss + hf * H2 + 4 * u, p.aligned & kAlDO) : make_uint4(0, 0, 0, 0);
+    qf[4 * u] = __uint_as_float(a.x); qf[4 * u + 1] = __uint_as_float(a.y);
+    qf[4 * u + 2] = __uint_as_float(a.z); qf[4 * u + 3] = __uint_as_float(a.w);
+    gf[4 * u] = __uint_as_float(b.x); gf[4 * u + 1] = __uint_as_float(b.y);
+    gf[4 * u + 2] = __uint_as_float(b.z); gf[4 * u + 3] = __uint_as_float(b.w);
+  }
+  float lse2 = __builtin_inff(), dl = 0.f;
+  if (qvalid) {
+    float l = p.lse.ptr[w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss];
+    lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    dl = p.delta[delta_index(s, w.b, w.h, g, qi)];
+  }
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  T ktile, vtile;
+  for (int t = kt0; t < kt1; ++t) {
+    const int kbase = t * BN;
+    ktile.load(kb, p.k.ss, kbase, g.sk, p.aligned & kAlK);
+    vtile.load(vb, p.v.ss, kbase, g.sk, p.aligned & kAlV);
+    __syncthreads();
+    ktile.store(sk_);
+    vtile.store(sv_);
+    __syncthreads();
+    if (kbase < wj1 && kbase + BN > wj0) {
+      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
+      f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+      for (int u = 0; u < H2 / 4; ++u) {
+        float4 kv = *reinterpret_cast<const float4*>(&sk_[l32 * T::RP + hf * H2 + 4 * u]);
+        float4 vv = *reinterpret_cast<const float4*>(&sv_[l32 * T::RP + hf * H2 + 4 * u]);
+        st = mfma32(kv.x, qf[4 * u], st); st = mfma32(kv.y, qf[4 * u + 1], st);
+        st = mfma32(kv.z, qf[4 * u + 2], st); st = mfma32(kv.w, qf[4 * u + 3], st);
+        dp = mfma32(vv.x, gf[4 * u], dp); dp = mfma32(vv.y, gf[4 * u + 1], dp);
+        dp = mfma32(vv.z, gf[4 * u + 2], dp); dp = mfma32(vv.w, gf[4 * u + 3], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(st[r] * s.scale_log2 - lse2);
+        if (!full && !visible(s, g, qi, kbase + 8 * (r >> 2) + 4 * hf + (r & 3))) pr = 0.f;
+        ds[r] = pr * (dp[r] - dl);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+          acc[db] = mfma32(sk_[key * T::RP + db * 32 + l32], ds[i], acc[db]);
+        }
+    }
+  }
+  if (qvalid) {
+    float* row = dqb + qi * p.dq.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float v[4] = {acc[db][4 * gq], acc[db][4 * gq + 1], acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+        out4_32(row + db * 32 + 8 * gq + 4 * hf, v, s.scale, p.aligned & kAlDQ, p.accumulate);
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
+  constexpr int BK = kBwdK, BQ = 32, H2 = D / 2, NDB = D / 32;
+  using T = Tile32<D>;
+  __shared__ __align__(16) float sq_[BQ * T::RP];
+  __shared__ __align__(16) float sg_[BQ * T::RP];
+  __shared__ __align__(16) float slse_[BQ];
+  __shared__ __align__(16) float sdl_[BQ];
+
+  const Shape& s = p.s;
+  BwdPos w;
+  if (!bwd_decode(s, p.work_k, p.count_k, s.hk, s.sk, BK, false, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int k0 = w.tile * BK;
+  if (k0 >= g.sk) return;
+  const int kend = min(k0 + BK, g.sk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int hk = w.h;
+  const float* kb = static_cast<const float*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const float* vb = static_cast<const float*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  float* dkb = static_cast<float*>(p.dk.ptr) + w.b * p.dk.sb + hk * p.dk.sh + g.krow0 * p.dk.ss;
+  float* dvb = static_cast<float*>(p.dv.ptr) + w.b * p.dv.sb + hk * p.dv.sh + g.krow0 * p.dv.ss;
+
+  int i0, i1;
+  query_range(s, g, k0, kend, i0, i1);
+  const int qt0 = i0 / BQ, qt1 = i1 > i0 ? (i1 + BQ - 1) / BQ : qt0;
+  const int kw0 = k0 + wave * 32, kw1 = min(kw0 + 32, g.sk);
+  const int kj = kw0 + l32;
+  const bool kvalid = kj < g.sk;
+  int wi0 = 0, wi1 = 0;
+  if (kw0 < kw1) query_range(s, g, kw0, kw1, wi0, wi1);
+
+  float kf[H2], vf[H2];
+#pragma unroll
+  for (int u = 0; u < H2 / 4; ++u) {
+    uint4 a = kvalid ? load16<4>(kb + kj * p.k.ss + hf * H2 + 4 * u, p.aligned & kAlK) : make_uint4(0, 0, 0, 0);
+    uint4 b = kvalid ? load16<4>(vb + kj * p.v.ss + hf * H2 + 4 * u, p.aligned & kAlV) : make_uint4(0, 0, 0, 0);
+    kf[4 * u] = __uint_as_float(a.x); kf[4 * u + 1] = __uint_as_float(a.y);
+    kf[4 * u + 2] = __uint_as_float(a.z); kf[4 * u + 3] = __uint_as_float(a.w);
+    vf[4 * u] = __uint_as_float(b.x); vf[4 * u + 1] = __uint_as_float(b.y);
+    vf[4 * u + 2] = __uint_as_float(b.z); vf[4 * u + 3] = __uint_as_float(b.w);
+  }
+  f32x16_t adk[NDB], adv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    adk[i] = zero16();
+    adv[i] = zero16();
+  }
+
+  T qtile, gtile;
+  for (int gi = 0; gi < s.group; ++gi) {
+    const int h = hk * s.group + gi;
+    const float* qb = static_cast<const float*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss;
+    const float* gb = static_cast<const float*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh + g.qrow0 * p.dout.ss;
+    for (int t = qt0; t < qt1; ++t) {
+      const int qbase = t * BQ;
+      qtile.load(qb, p.q.ss, qbase, g.sq, p.aligned & kAlQ);
+      gtile.load(gb, p.dout.ss, qbase, g.sq, p.aligned & kAlDO);
+      float lv = __builtin_inff(), dv = 0.f;
+      if (tid < BQ) {
+        int i = qbase + tid;
+        if (i < g.sq) {
+          float l = p.lse.ptr[w.b * p.lse.sb + h * p.lse.sh + (g.qrow0 + i) * p.lse.ss];
+          lv = l == kNegInf ? __builtin_inff() : l * kLog2e;
+          dv = p.delta[delta_index(s, w.b, h, g, i)];
+        }
+      }
+      __syncthreads();
+      qtile.store(sq_);
+      gtile.store(sg_);
+      if (tid < BQ) {
+        slse_[tid] = lv;
+        sdl_[tid] = dv;
+      }
+      __syncthreads();
+      if (qbase < wi1 && qbase + BQ > wi0) {
+        const bool full = tile_full(s, g, qbase, min(qbase + BQ, g.sq), kw0, kw1);
+        f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+        for (int u = 0; u < H2 / 4; ++u) {
+          float4 qv = *reinterpret_cast<const float4*>(&sq_[l32 * T::RP + hf * H2 + 4 * u]);
+          float4 gv = *reinterpret_cast<const float4*>(&sg_[l32 * T::RP + hf * H2 + 4 * u]);
+          st = mfma32(qv.x, kf[4 * u], st); st = mfma32(qv.y, kf[4 * u + 1], st);
+          st = mfma32(qv.z, kf[4 * u + 2], st); st = mfma32(qv.w, kf[4 * u + 3], st);
+          dp = mfma32(gv.x, vf[4 * u], dp); dp = mfma32(gv.y, vf[4 * u + 1], dp);
+          dp = mfma32(gv.z, vf[4 * u + 2], dp); dp = mfma32(gv.w, vf[4 * u + 3], dp);
+        }
+        float pr[16], ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 8 * (r >> 2) + 4 * hf + (r & 3);
+          float x = fast_exp2(st[r] * s.scale_log2 - slse_[ql]);
+          if (!full && !visible(s, g, qbase + ql, kj)) x = 0.f;
+          pr[r] = x;
+          ds[r] = x * (dp[r] - sdl_[ql]);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ql = 8 * (i >> 2) + 4 * hf + (i & 3);
+            adv[db] = mfma32(sg_[ql * T::RP + db * 32 + l32], pr[i], adv[db]);
+            adk[db] = mfma32(sq_[ql * T::RP + db * 32 + l32], ds[i], adk[db]);
+          }
+      }
+    }
+  }
+  if (kvalid) {
+    float* krow = dkb + kj * p.dk.ss;
+    float* vrow = dvb + kj * p.dv.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = db * 32 + 8 * gq + 4 * hf;
+        float a[4] = {adk[db][4 * gq], adk[db][4 * gq + 1], adk[db][4 * gq + 2], adk[db][4 * gq + 3]};
+        float b2[4] = {adv[db][4 * gq], adv[db][4 * gq + 1], adv[db][4 * gq + 2], adv[db][4 * gq + 3]};
+        out4_32(krow + d, a, s.scale, p.aligned & kAlDK, p.accumulate);
+        out4_32(vrow + d, b2, 1.f, p.aligned & kAlDV, p.accumulate);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// launches
+// ----------------------------------------------------------------------------------------
+template <class K>
+static hipError_t go(K kernel, const char* name, int64_t blocks, hipStream_t st, const BwdParams& p) {
+  if (blocks <= 0) return hipSuccess;
+  prof_begin(st, name);
+  hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  prof_end(st);
+  return hipGetLastError();
+}
+
+template <int ES, bool BF>
+static hipError_t pre(const BwdParams& p, hipStream_t st) {
+  const Shape& s = p.s;
+  int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
+  auto launch = [&](auto kernel, int d) {
+    int rpb = kThreads / (d / (16 / ES));
+    return go(kernel, "bwd_pre", (rows + rpb - 1) / rpb, st, p);
+  };
+  if (s.d == 32) return launch(bwd_pre_kernel<ES, BF, 32>, 32);
+  if (s.d == 64) return launch(bwd_pre_kernel<ES, BF, 64>, 64);
+  return launch(bwd_pre_kernel<ES, BF, 128>, 128);
+}
+
+template <bool BF, int D>
+static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t bk) {
+  hipError_t e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+  if (e != hipSuccess) return e;
+  return go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
+}
+
+template <int D>
+static hipError_t main32(const BwdParams& p, hipStream_t st, int64_t bq, int64_t bk) {
+  hipError_t e = go(bwd_dkdv32_kernel<D>, "bwd_dkdv", bk, st, p);
+  if (e != hipSuccess) return e;
+  return go(bwd_dq32_kernel<D>, "bwd_dq", bq, st, p);
+}
+
+hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
+  const Shape& s = p.s;
+  hipError_t e = dt == DType::F32 ? pre<4, false>(p, st)
+                                   : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
+  if (e != hipSuccess) return e;
+  int64_t bq = s.thd ? ((s.total_q + kBwdQ - 1) / kBwdQ + s.batch) * s.hq
+                     : int64_t((s.sq + kBwdQ - 1) / kBwdQ) * s.batch * s.hq;
+  int64_t bk = s.thd ? ((s.total_k + kBwdK - 1) / kBwdK + s.batch) * s.hk
+                     : int64_t((s.sk + kBwdK - 1) / kBwdK) * s.batch * s.hk;
+  switch (dt) {
+    case DType::BF16:
+      if (s.d == 32) return main16<true, 32>(p, st, bq, bk);
+      if (s.d == 64) return main16<true, 64>(p, st, bq, bk);
+      return main16<true, 128>(p, st, bq, bk);
+    case DType::F16:
+      if (s.d == 32) return main16<false, 32>(p, st, bq, bk);
+      if (s.d == 64) return main16<false, 64>(p, st, bq, bk);
+      return main16<false, 128>(p, st, bq, bk);
+    default:
+      if (s.d == 32) return main32<32>(p, st, bq, bk);
+      if (s.d == 64) return main32<64>(p, st, bq, bk);
+      return main32<128>(p, st, bq, bk);
+  }
+}
+
+}  // namespace sdpa

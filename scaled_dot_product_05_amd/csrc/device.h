@@ -1,0 +1,205 @@
+// Device helpers shared by the gfx950 kernels: MFMA wrappers, conversions, strided row
+// loads, per-sequence geometry and the window predicate.
+//
+// MFMA operand layouts used throughout (wave64, v_mfma_f32_32x32x16_{bf16,f16}):
+//   A (32 x 16): lane l holds row l%32, contraction slots 8*(l/32) .. 8*(l/32)+7
+//   B (16 x 32): lane l holds column l%32, contraction slots 8*(l/32) .. +7
+//   C (32 x 32): lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
+// and for v_mfma_f32_32x32x2_f32 one fp32 per lane, contraction slot l/32.
+// A C tile therefore serves directly as the B operand of a product that contracts over
+// its rows, once both operands agree on which row each contraction slot holds.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "params.h"
+#include "tiles.h"
+
+namespace sdpa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <bool BF>
+__device__ __forceinline__ f32x16_t mfma16(const uint4& a, const uint4& b, const f32x16_t& c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(float a, float b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f64_16x16x4_f64: fp64 inputs and accumulation.  A: lane l holds row l%16, slot
+// l/16; B: column l%16, slot l/16; C: register r of lane l holds row 4*r + l/16, column l%16.
+__device__ __forceinline__ f64x4_t mfma64(double a, double b, const f64x4_t& c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x4_f32.  A and B as the fp64 form; C: register r of lane l holds row
+// 4*(l/16) + r, column l%16.
+__device__ __forceinline__ f32x4_t mfma16x4(float a, float b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f64x4_t zero4d() { return f64x4_t{0.0, 0.0, 0.0, 0.0}; }
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Round two fp32 values to the 16-bit type (round to nearest even) and pack lo | hi << 16.
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  if constexpr (BF) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+template <bool BF>
+__device__ __forceinline__ float to_f32(uint16_t x) {
+  if constexpr (BF) return __uint_as_float(uint32_t(x) << 16);
+  else return float(__builtin_bit_cast(_Float16, x));
+}
+
+template <bool BF>
+__device__ __forceinline__ uint16_t from_f32(float x) {
+  if constexpr (BF) return __builtin_bit_cast(uint16_t, __bf16(x));
+  else return __builtin_bit_cast(uint16_t, _Float16(x));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// 16 bytes from a row that is 16-byte aligned (al) or only element aligned.
+template <int ES>
+__device__ __forceinline__ uint4 load16(const void* p, bool al) {
+  if (al) return *static_cast<const uint4*>(p);
+  uint4 r;
+  if constexpr (ES == 2) {
+    const uint16_t* e = static_cast<const uint16_t*>(p);
+    r.x = uint32_t(e[0]) | (uint32_t(e[1]) << 16);
+    r.y = uint32_t(e[2]) | (uint32_t(e[3]) << 16);
+    r.z = uint32_t(e[4]) | (uint32_t(e[5]) << 16);
+    r.w = uint32_t(e[6]) | (uint32_t(e[7]) << 16);
+  } else {
+    const uint32_t* e = static_cast<const uint32_t*>(p);
+    r.x = e[0]; r.y = e[1]; r.z = e[2]; r.w = e[3];
+  }
+  return r;
+}
+
+template <int ES>
+__device__ __forceinline__ void store16(void* p, const uint4& v, bool al) {
+  if (al) { *static_cast<uint4*>(p) = v; return; }
+  if constexpr (ES == 2) {
+    uint16_t* e = static_cast<uint16_t*>(p);
+    e[0] = v.x; e[1] = v.x >> 16; e[2] = v.y; e[3] = v.y >> 16;
+    e[4] = v.z; e[5] = v.z >> 16; e[6] = v.w; e[7] = v.w >> 16;
+  } else {
+    uint32_t* e = static_cast<uint32_t*>(p);
+    e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+  }
+}
+
+// 8 bytes (four 16-bit elements) to a row.
+__device__ __forceinline__ void store8(uint16_t* p, uint32_t lo, uint32_t hi, bool al) {
+  if (al) { *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi); return; }
+  p[0] = lo; p[1] = lo >> 16; p[2] = hi; p[3] = hi >> 16;
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// 16-bit element e (0..7) of a 16-byte vector.
+__device__ __forceinline__ uint32_t elem16(const uint4& v, int e) {
+  return (u4get(v, e >> 1) >> ((e & 1) * 16)) & 0xffffu;
+}
+
+// Position of key (or query) row `r` inside a transposed 16-bit LDS tile: bits 2 and 3
+// swapped, so that the 8 contraction slots a lane feeds to one MFMA are contiguous.
+__host__ __device__ __forceinline__ int tpos(int r) {
+  return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// One sequence of the batch: first packed row (THD) and its lengths.
+struct Seq {
+  int64_t qrow0, krow0;
+  int32_t sq, sk, off;
+};
+
+__device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+__device__ __forceinline__ Seq seq_of(const Shape& s, int b) {
+  Seq r;
+  if (s.thd) {
+    int64_t a0 = clamp64(s.cu_q[b], 0, s.total_q);
+    int64_t a1 = clamp64(s.cu_q[b + 1], a0, s.total_q);
+    int64_t c0 = clamp64(s.cu_k[b], 0, s.total_k);
+    int64_t c1 = clamp64(s.cu_k[b + 1], c0, s.total_k);
+    r.qrow0 = a0;
+    r.krow0 = c0;
+    r.sq = int32_t(a1 - a0 < s.sq ? a1 - a0 : s.sq);
+    r.sk = int32_t(c1 - c0 < s.sk ? c1 - c0 : s.sk);
+  } else {
+    r.qrow0 = 0;
+    r.krow0 = 0;
+    r.sq = s.sq;
+    r.sk = s.sk;
+  }
+  r.off = s.bottom_right ? r.sk - r.sq : 0;
+  return r;
+}
+
+// Keys [j0, j1) that some query in rows [i0, i1) may see (i1 > i0).
+__device__ __forceinline__ void key_range(const Shape& s, const Seq& g, int i0, int i1, int& j0,
+                                          int& j1) {
+  int64_t lo = int64_t(i0) + g.off + s.lo_rel;
+  int64_t hi = int64_t(i1 - 1) + g.off + s.hi_rel + 1;
+  j0 = int(clamp64(lo, 0, g.sk));
+  j1 = int(clamp64(hi, j0, g.sk));
+}
+
+// Queries [i0, i1) that may see some key in [j0, j1) (j1 > j0).
+__device__ __forceinline__ void query_range(const Shape& s, const Seq& g, int j0, int j1, int& i0,
+                                            int& i1) {
+  int64_t lo = int64_t(j0) - g.off - s.hi_rel;
+  int64_t hi = int64_t(j1 - 1) - g.off - s.lo_rel + 1;
+  i0 = int(clamp64(lo, 0, g.sq));
+  i1 = int(clamp64(hi, i0, g.sq));
+}
+
+__device__ __forceinline__ bool visible(const Shape& s, const Seq& g, int i, int j) {
+  int rel = j - i - g.off;
+  return rel >= s.lo_rel && rel <= s.hi_rel && j < g.sk && i < g.sq;
+}
+
+// Every (i, j) of rows [i0, i1) x keys [j0, j1) visible and in range.
+__device__ __forceinline__ bool tile_full(const Shape& s, const Seq& g, int i0, int i1, int j0,
+                                          int j1) {
+  return int64_t(j0) - (i1 - 1) - g.off >= s.lo_rel && int64_t(j1 - 1) - i0 - g.off <= s.hi_rel &&
+         j1 <= g.sk && i1 <= g.sq;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,472 @@
+// Fused attention forward for gfx950: O = softmax(scale Q K^T + mask) V and LSE.
+//
+// The method (online softmax over key tiles, LSE = m + log l) reaches the plain
+// definition exactly up to rounding; the pages define the result, not the tiling:
+// "Significant Accuracy Difference between Compiled and Eager Flex Attention" (PyTorch
+// issue 135161, return_lse and merge_attn) and "[PyTorch] fused CUDNN attention kernel not
+// properly handling strides" (TransformerEngine issue 1195, strided packed q/k/v, causal
+// window (-1,0), softmax_scale, MQA/GQA).
+//
+// One workgroup (4 waves) owns 128 query rows of one (sequence, q head); each wave owns 32
+// of them.  The wave computes S^T = K Q^T for a 32-key block with the query as the MFMA
+// column, so each lane holds one query and 16 of its keys: the row max and row sum are
+// in-lane reductions plus one exchange with the lane 32 away.  P^T then feeds O^T += V^T P^T
+// straight from registers.  K tiles sit in LDS row-major; V tiles are transposed on the way
+// into LDS so a lane's 8 contraction keys are one 16-byte read.  K/V tiles are double
+// buffered: the global loads of tile t+1 are in flight while tile t is computed.
+// Key tiles outside the window are never visited; only tiles that straddle the window edge
+// or the sequence end evaluate the mask.  Work is issued longest-first (for causal masks the
+// last query tiles see the most keys).
+#include "device.h"
+#include "launch.h"
+#include "profile.h"
+
+namespace sdpa {
+
+struct WorkPos {
+  int b, h, tile;
+};
+
+// Decode blockIdx.x into (sequence, q head, q tile).  Returns false for idle blocks.
+__device__ __forceinline__ bool decode_work(const Shape& s, const WorkItem* work,
+                                            const int32_t* count, int rows_per_tile, WorkPos& w) {
+  if (s.thd) {
+    int item = blockIdx.x / s.hq;
+    w.h = blockIdx.x % s.hq;
+    if (item >= *count) return false;
+    WorkItem it = work[item];
+    w.b = it.seq;
+    w.tile = it.tile;
+    return true;
+  }
+  int bh = s.batch * s.hq;
+  int nt = (s.sq + rows_per_tile - 1) / rows_per_tile;
+  int t = blockIdx.x / bh;
+  int r = blockIdx.x % bh;
+  w.b = r / s.hq;
+  w.h = r % s.hq;
+  w.tile = nt - 1 - t;
+  return true;
+}
+
+// ----------------------------------------------------------------------------------------
+// bf16 / fp16 inputs: MFMA 32x32x16, fp32 accumulation
+// ----------------------------------------------------------------------------------------
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
+  constexpr int BM = kFwdBM, BN = kFwdBN16;
+  constexpr int KP = D + 8;   // K row pitch in elements (+16 B: conflict-free 16 B reads)
+  constexpr int VP = BN + 8;  // V^T row pitch
+  constexpr int NC = D / 16;  // contraction chunks of Q K^T
+  constexpr int NKB = BN / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NPC = BN / 16;  // contraction chunks of P V
+  constexpr int LDC = BN * D / 8 / kThreads;  // 16-byte chunks per thread per tile
+  static_assert(LDC >= 1 && LDC <= 4, "tile split");
+  __shared__ __align__(16) uint16_t sk_[2][BN * KP];
+  __shared__ __align__(16) uint16_t sv_[2][D * VP];
+
+  const Shape& s = p.s;
+  WorkPos w;
+  if (!decode_work(s, p.work, p.work_count, BM, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int hk = w.h / s.group;
+
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh +
+                       g.qrow0 * p.q.ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh +
+                       g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh +
+                       g.krow0 * p.v.ss;
+  uint16_t* ob = static_cast<uint16_t*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
+  const bool alq = p.aligned & kAlQ, alk = p.aligned & kAlK, alv = p.aligned & kAlV,
+             alo = p.aligned & kAlO;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN;
+  const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+
+  const int qw0 = q0 + wave * 32;
+  const int qw1 = min(qw0 + 32, g.sq);
+  const int qi = qw0 + l32;
+  const bool qvalid = qi < g.sq;
+  int wj0 = 0, wj1 = 0;
+  if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+
+  uint4 qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qf[c] = qvalid ? load16<2>(qb + qi * p.q.ss + 16 * c + 8 * hf, alq) : make_uint4(0, 0, 0, 0);
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+  float m_run = kNegInf, l_run = 0.f;
+
+  uint4 kst[LDC], vst[LDC];
+  const int vdc = tid % (D / 8), vkg = tid / (D / 8);
+  auto gload = [&](int kt) {
+    const int base = kt * BN;
+#pragma unroll
+    for (int u = 0; u < LDC; ++u) {
+      int ci = tid + u * kThreads;
+      int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      int j = base + row;
+      kst[u] = j < g.sk ? load16<2>(kb + j * p.k.ss + col, alk) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < LDC; ++x) {
+      int j = base + vkg * LDC + x;
+      vst[x] = j < g.sk ? load16<2>(vb + j * p.v.ss + vdc * 8, alv) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LDC; ++u) {
+      int ci = tid + u * kThreads;
+      int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&sk_[buf][row * KP + col]) = kst[u];
+    }
+    // V^T: this thread's LDC keys x 8 d, written as 8 rows of LDC contiguous keys
+    const int pos = tpos(vkg * LDC);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t* dst = &sv_[buf][(vdc * 8 + e) * VP + pos];
+      if constexpr (LDC == 4) {
+        uint32_t lo = elem16(vst[0], e) | (elem16(vst[1], e) << 16);
+        uint32_t hi = elem16(vst[2], e) | (elem16(vst[3], e) << 16);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      } else if constexpr (LDC == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = elem16(vst[0], e) | (elem16(vst[1], e) << 16);
+      } else {
+        *dst = uint16_t(elem16(vst[0], e));
+      }
+    }
+  };
+
+  if (kt0 < kt1) {
+    gload(kt0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) gload(kt + 1);
+    const int kbase = kt * BN;
+    if (kbase < wj1 && kbase + BN > wj0) {
+      f32x16_t st[NKB];
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2) {
+        st[k2] = zero16();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          uint4 a = *reinterpret_cast<const uint4*>(&sk_[buf][(k2 * 32 + l32) * KP + 16 * c + 8 * hf]);
+          st[k2] = mfma16<BF>(a, qf[c], st[k2]);
+        }
+      }
+      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
+      float mx = kNegInf;
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = st[k2][r] * s.scale_log2;
+          if (!full) {
+            int j = kbase + k2 * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (!visible(s, g, qi, j)) x = kNegInf;
+          }
+          st[k2][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float ps = 0.f;
+      uint4 pf[NPC];
+#pragma unroll
+      for (int c = 0; c < NPC; ++c) {
+        const int k2 = c >> 1, rb = (c & 1) * 8;
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = fast_exp2(st[k2][rb + j] - m_use);
+          ps += e[j];
+        }
+        pf[c] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
+                           pack2<BF>(e[6], e[7]));
+      }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+#pragma unroll
+        for (int c = 0; c < NPC; ++c) {
+          uint4 a = *reinterpret_cast<const uint4*>(&sv_[buf][(db * 32 + l32) * VP + 16 * c + 8 * hf]);
+          acc[db] = mfma16<BF>(a, pf[c], acc[db]);
+        }
+      }
+    }
+    if (more) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = l_run + xor32(l_run);
+  if (qvalid) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = ob + qi * p.o.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        int d = db * 32 + 8 * gq + 4 * hf;
+        uint32_t lo = pack2<BF>(acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv);
+        uint32_t hi = pack2<BF>(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv);
+        store8(orow + d, lo, hi, alo);
+      }
+    }
+    if (hf == 0 && p.lse.ptr) {
+      float* lp = p.lse.ptr + w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
+      *lp = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// fp32 inputs.  Nothing is rounded below fp32 (PyTorch issue 135161 traces its large
+// gradient errors to a tensor-core shortcut inside an "fp32" kernel), and the scores are
+// formed in fp64: fp32 inputs widen exactly, v_mfma_f64_16x16x4 accumulates q.k in fp64,
+// and the row max is subtracted in fp64 before the fp32 exp2.  With the pages' fp32
+// local/global workload (q, k, v from a Linear layer filled with 0.1) scores reach ~2e2,
+// where fp32 score rounding alone moves O by ~1e-5.  P V uses fp32 MFMA 16x16x4.
+//
+// 16x16 tiles: v_mfma_{f64_16x16x4_f64, f32_16x16x4_f32} put lane l on column l%16 and
+// contraction slot l/16.  Their C layouts differ: register r of lane l is row 4*r + l/16
+// for the fp64 form and row 4*(l/16) + r for the fp32 form.  Each wave owns 32 queries
+// (two 16-column blocks); a K/V tile is 32 keys (two 16-row blocks).
+// ----------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdParams p) {
+  constexpr int BM = kFwdBM, BN = kFwdBN32;
+  constexpr int KP = D + 4;  // row pitch in floats
+  constexpr int Q4 = D / 4;  // d values per contraction slot group
+  constexpr int NDB = D / 16;
+  constexpr int LDC = BN * D / 4 / kThreads;
+  static_assert(BN == 32 && LDC >= 1, "tile split");
+  __shared__ __align__(16) float sk_[2][BN * KP];
+  __shared__ __align__(16) float sv_[2][BN * KP];
+
+  const Shape& s = p.s;
+  WorkPos w;
+  if (!decode_work(s, p.work, p.work_count, BM, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, sg = lane >> 4;
+  const int hk = w.h / s.group;
+
+  const float* qb = static_cast<const float*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh + g.qrow0 * p.q.ss;
+  const float* kb = static_cast<const float*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const float* vb = static_cast<const float*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  float* ob = static_cast<float*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
+  const bool alq = p.aligned & kAlQ, alk = p.aligned & kAlK, alv = p.aligned & kAlV,
+             alo = p.aligned & kAlO;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN;
+  const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  const int qw0 = q0 + wave * 32;
+  const int qw1 = min(qw0 + 32, g.sq);
+  int wj0 = 0, wj1 = 0;
+  if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+  const double scale = double(s.scale);
+  const double log2e = 1.4426950408889634;
+
+  float qf[2][Q4];
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2) {
+    const int qi = qw0 + 16 * qb2 + l16;
+#pragma unroll
+    for (int u = 0; u < Q4 / 4; ++u) {
+      uint4 t = qi < g.sq ? load16<4>(qb + qi * p.q.ss + sg * Q4 + 4 * u, alq) : make_uint4(0, 0, 0, 0);
+      qf[qb2][4 * u] = __uint_as_float(t.x);
+      qf[qb2][4 * u + 1] = __uint_as_float(t.y);
+      qf[qb2][4 * u + 2] = __uint_as_float(t.z);
+      qf[qb2][4 * u + 3] = __uint_as_float(t.w);
+    }
+  }
+  f32x4_t acc[NDB][2];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i][0] = acc[i][1] = zero4();
+  double m_run[2] = {-__builtin_inf(), -__builtin_inf()};
+  float l_run[2] = {0.f, 0.f};
+
+  uint4 kst[LDC], vst[LDC];
+  auto gload = [&](int kt) {
+    const int base = kt * BN;
+#pragma unroll
+    for (int u = 0; u < LDC; ++u) {
+      int ci = tid + u * kThreads;
+      int row = ci / (D / 4), col = (ci % (D / 4)) * 4;
+      int j = base + row;
+      bool in = j < g.sk;
+      kst[u] = in ? load16<4>(kb + j * p.k.ss + col, alk) : make_uint4(0, 0, 0, 0);
+      vst[u] = in ? load16<4>(vb + j * p.v.ss + col, alv) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LDC; ++u) {
+      int ci = tid + u * kThreads;
+      int row = ci / (D / 4), col = (ci % (D / 4)) * 4;
+      *reinterpret_cast<uint4*>(&sk_[buf][row * KP + col]) = kst[u];
+      *reinterpret_cast<uint4*>(&sv_[buf][row * KP + col]) = vst[u];
+    }
+  };
+
+  if (kt0 < kt1) {
+    gload(kt0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) gload(kt + 1);
+    const int kbase = kt * BN;
+    if (kbase < wj1 && kbase + BN > wj0) {
+      // S^T blocks (key block kb, query block qb) in fp64
+      f64x4_t st[2][2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) st[a][0] = st[a][1] = zero4d();
+#pragma unroll
+      for (int u = 0; u < Q4 / 4; ++u) {
+        float4 kv[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          kv[k2] = *reinterpret_cast<const float4*>(&sk_[buf][(16 * k2 + l16) * KP + sg * Q4 + 4 * u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const double kd = double(e == 0 ? kv[k2].x : e == 1 ? kv[k2].y : e == 2 ? kv[k2].z : kv[k2].w);
+#pragma unroll
+            for (int qb2 = 0; qb2 < 2; ++qb2) st[k2][qb2] = mfma64(kd, double(qf[qb2][4 * u + e]), st[k2][qb2]);
+          }
+        }
+      }
+      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2) {
+        const int qi = qw0 + 16 * qb2 + l16;
+        double mx = -__builtin_inf();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            double t = st[k2][qb2][r] * scale;
+            if (!full && !visible(s, g, qi, kbase + 16 * k2 + 4 * r + sg)) t = -__builtin_inf();
+            st[k2][qb2][r] = t;
+            mx = fmax(mx, t);
+          }
+        mx = fmax(mx, __shfl_xor(mx, 16));
+        mx = fmax(mx, __shfl_xor(mx, 32));
+        const double m_new = fmax(m_run[qb2], mx);
+        const double m_use = m_new == -__builtin_inf() ? 0.0 : m_new;
+        const float alpha = fast_exp2(float((m_run[qb2] - m_use) * log2e));
+        float ps = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float e = fast_exp2(float((st[k2][qb2][r] - m_use) * log2e));
+            st[k2][qb2][r] = e;  // P^T kept in the fp64 slots, exact in fp32
+            ps += e;
+          }
+        l_run[qb2] = l_run[qb2] * alpha + ps;
+        m_run[qb2] = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[db][qb2][r] *= alpha;
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[db][qb2] = mfma16x4(sv_[buf][(16 * k2 + 4 * r + sg) * KP + 16 * db + l16],
+                                      float(st[k2][qb2][r]), acc[db][qb2]);
+        }
+      }
+    }
+    if (more) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2) {
+    float lt = l_run[qb2];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int qi = qw0 + 16 * qb2 + l16;
+    if (qi < g.sq) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* orow = ob + qi * p.o.ss;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        uint4 v = make_uint4(__float_as_uint(acc[db][qb2][0] * inv), __float_as_uint(acc[db][qb2][1] * inv),
+                             __float_as_uint(acc[db][qb2][2] * inv), __float_as_uint(acc[db][qb2][3] * inv));
+        store16<4>(orow + 16 * db + 4 * sg, v, alo);
+      }
+      if (sg == 0 && p.lse.ptr) {
+        float* lp = p.lse.ptr + w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
+        *lp = lt > 0.f ? float(m_run[qb2] + double(__logf(lt))) : kNegInf;
+      }
+    }
+  }
+}
+
+template <class K>
+static hipError_t go(K kernel, int blocks, hipStream_t st, const FwdParams& p) {
+  prof_begin(st, "attn_fwd");
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, st, p);
+  prof_end(st);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdParams& p, DType dt, hipStream_t st) {
+  const Shape& s = p.s;
+  int64_t blocks = s.thd ? (s.total_q + kFwdBM - 1) / kFwdBM + s.batch
+                         : int64_t((s.sq + kFwdBM - 1) / kFwdBM) * s.batch;
+  blocks *= s.hq;
+  if (blocks <= 0) return hipSuccess;
+  int nb = int(blocks);
+  switch (dt) {
+    case DType::BF16:
+      if (s.d == 32) return go(fwd16_kernel<true, 32>, nb, st, p);
+      if (s.d == 64) return go(fwd16_kernel<true, 64>, nb, st, p);
+      return go(fwd16_kernel<true, 128>, nb, st, p);
+    case DType::F16:
+      if (s.d == 32) return go(fwd16_kernel<false, 32>, nb, st, p);
+      if (s.d == 64) return go(fwd16_kernel<false, 64>, nb, st, p);
+      return go(fwd16_kernel<false, 128>, nb, st, p);
+    default:
+      if (s.d == 32) return go(fwd32_kernel<32>, nb, st, p);
+      if (s.d == 64) return go(fwd32_kernel<64>, nb, st, p);
+      return go(fwd32_kernel<128>, nb, st, p);
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,112 @@
+// Varlen (THD) scheduler: turns device cu_seqlens into a work list of (sequence, tile)
+// items, most expensive first, so that the long causal tiles of the long sequences start
+// before the short ones fill the machine.  Packed THD sequences with int32 cu_seqlens come
+// from "Add support for cuDNN FusedAttention + THD + CP" (TransformerEngine issue 885).
+//
+// One workgroup: histogram of item costs (cost = number of tiles on the other side that
+// the window lets the item see), an exclusive scan of the histogram from the most to the
+// least expensive bucket, then a scatter through LDS atomic counters.  The order inside a
+// bucket does not matter: every item writes its own output rows.
+#include "device.h"
+#include "launch.h"
+#include "profile.h"
+
+namespace sdpa {
+
+constexpr int kSchedThreads = 1024;
+
+struct SeqLens {
+  int own, other, off;  // lengths and the diagonal offset of this sequence
+};
+
+__device__ __forceinline__ SeqLens sched_lens(const SchedParams& p, int b) {
+  int64_t a0 = clamp64(p.cu_own[b], 0, p.total_own);
+  int64_t a1 = clamp64(p.cu_own[b + 1], a0, p.total_own);
+  int64_t c0 = clamp64(p.cu_other[b], 0, p.total_other);
+  int64_t c1 = clamp64(p.cu_other[b + 1], c0, p.total_other);
+  SeqLens r;
+  r.own = int(min<int64_t>(a1 - a0, p.max_own));
+  r.other = int(min<int64_t>(c1 - c0, p.max_other));
+  int sq = p.own_is_query ? r.own : r.other;
+  int sk = p.own_is_query ? r.other : r.own;
+  r.off = p.bottom_right ? sk - sq : 0;
+  return r;
+}
+
+__device__ __forceinline__ int item_cost(const SchedParams& p, const SeqLens& L, int t) {
+  int r0 = t * p.tile_own;
+  int r1 = min(r0 + p.tile_own, L.own);
+  int64_t lo, hi;
+  if (p.own_is_query) {  // keys seen by query rows [r0, r1)
+    lo = int64_t(r0) + L.off + p.lo_rel;
+    hi = int64_t(r1 - 1) + L.off + p.hi_rel + 1;
+  } else {  // queries that see key rows [r0, r1)
+    lo = int64_t(r0) - L.off - p.hi_rel;
+    hi = int64_t(r1 - 1) - L.off - p.lo_rel + 1;
+  }
+  lo = clamp64(lo, 0, L.other);
+  hi = clamp64(hi, lo, L.other);
+  if (hi <= lo) return 0;
+  int64_t c = (hi + p.tile_other - 1) / p.tile_other - lo / p.tile_other;
+  return int(min<int64_t>(c, kSchedBuckets - 1));
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
+  __shared__ int hist[kSchedBuckets];
+  __shared__ int part[kSchedThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int nwaves = kSchedThreads / 64;
+  constexpr int PER = kSchedBuckets / kSchedThreads;
+  for (int i = tid; i < kSchedBuckets; i += kSchedThreads) hist[i] = 0;
+  __syncthreads();
+  for (int b = wave; b < p.batch; b += nwaves) {
+    SeqLens L = sched_lens(p, b);
+    int nt = (L.own + p.tile_own - 1) / p.tile_own;
+    for (int t = lane; t < nt; t += 64) atomicAdd(&hist[item_cost(p, L, t)], 1);
+  }
+  __syncthreads();
+  // exclusive scan in decreasing cost order: thread i owns reversed buckets PER*i .. PER*i+PER-1
+  int local = 0;
+  for (int k = 0; k < PER; ++k) local += hist[kSchedBuckets - 1 - (PER * tid + k)];
+  part[tid] = local;
+  __syncthreads();
+  for (int step = 1; step < kSchedThreads; step <<= 1) {
+    int v = tid >= step ? part[tid - step] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - local;  // exclusive prefix of this thread's first bucket
+  const int total = part[kSchedThreads - 1];
+  __syncthreads();
+  for (int k = 0; k < PER; ++k) {
+    int c = kSchedBuckets - 1 - (PER * tid + k);
+    int n = hist[c];
+    hist[c] = run;  // becomes the next free slot of bucket c
+    run += n;
+  }
+  __syncthreads();
+  for (int b = wave; b < p.batch; b += nwaves) {
+    SeqLens L = sched_lens(p, b);
+    int nt = (L.own + p.tile_own - 1) / p.tile_own;
+    for (int t = lane; t < nt; t += 64) {
+      int pos = atomicAdd(&hist[item_cost(p, L, t)], 1);
+      if (pos < p.max_items) {
+        WorkItem it;
+        it.seq = b;
+        it.tile = t;
+        p.items[pos] = it;
+      }
+    }
+  }
+  if (tid == 0) *p.count = min(total, p.max_items);
+}
+
+hipError_t launch_schedule(const SchedParams& p, hipStream_t st) {
+  prof_begin(st, "thd_schedule");
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, p);
+  prof_end(st);
+  return hipGetLastError();
+}
+
+}  // namespace sdpa
