@@ -84,7 +84,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra measurements")
+    ap.add_argument("--workload", choices=("c2", "target"), default="c2",
+                    help="c2: causal bf16 fwd+bwd B4 S1024 H8 D64 (default); target: causal bf16 "
+                         "forward only, B8 S4096 H8 D64 (for profiling the forward kernel)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode; run with --gpus 1)", file=sys.stderr)
@@ -99,8 +106,10 @@ def main() -> int:
     S.lib()
 
     # ---------------- the step: causal bf16 fwd + bwd, B4 S1024 H8 D64 ----------------
-    w = synth.c2()
-    q, k, v, g = (t.to(dev) for t in (w.q, w.k, w.v, w.dout))
+    fwd_only = args.workload == "target"
+    w = synth.target() if fwd_only else synth.c2()
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    g = torch.empty_like(q) if fwd_only else w.dout.to(dev)
     pr = S.Problem(q, k, "bshd", w.scale, w.window)
     o = torch.empty_like(q)
     lse = torch.empty(pr.lse_shape, dtype=torch.float32, device=dev)
@@ -116,14 +125,14 @@ def main() -> int:
 
     def step():
         r1 = lib.sdpa_fwd(ctypes.byref(desc), hq, hk, hv, ho, hl, None, 0, stream)
-        r2 = lib.sdpa_bwd(ctypes.byref(desc), hq, hk, hv, ho, hl, hg, hnull, hdq, hdk, hdv, 0,
-                          wsp, wsn, stream)
+        r2 = 0 if fwd_only else lib.sdpa_bwd(ctypes.byref(desc), hq, hk, hv, ho, hl, hg, hnull,
+                                             hdq, hdk, hdv, 0, wsp, wsn, stream)
         if r1 or r2:
             raise S.SdpaError(r1 or r2, lib.sdpa_last_error().decode())
 
     nvis = w.batch * w.heads_q * S.n_visible(w.seqlen_q, w.seqlen_k, w.window)
     d = w.head_dim
-    flops_step = S.flops(nvis, d) + S.flops(nvis, d, backward=True)
+    flops_step = S.flops(nvis, d) + (0 if fwd_only else S.flops(nvis, d, backward=True))
     alg_flops = {"attn_fwd": 4 * d * nvis, "bwd_dkdv": 8 * d * nvis, "bwd_dq": 2 * d * nvis}
 
     log(f"warmup {args.warmup} steps")
@@ -153,24 +162,26 @@ def main() -> int:
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3),
                 "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_TFLOPS["bf16"], 5),
-                "traffic": traffic_for(dom, "c2"), "avg_launch_ms": round(dom_ms, 6),
+                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": round(dom_ms, 6),
                 "algorithmic_flops_per_launch": alg_flops[dom]}
     else:
         nbytes = 2 * w.batch * w.seqlen_q * w.heads_q * d * 2 + w.batch * w.heads_q * w.seqlen_q * 4
         ach = nbytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 5),
-                "traffic": traffic_for(dom, "c2"), "avg_launch_ms": round(dom_ms, 6)}
+                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": round(dom_ms, 6)}
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal self-attention fwd+bwd, bf16, B4 S1024 H8 D64, BSHD "
-                               "contiguous, scale 1/8, N(0,1) inputs",
-                   "batch": 4, "seq_len": 1024, "heads": 8, "head_dim": 64, "mask": "causal",
-                   "flops_per_step": flops_step},
+        "config": {"workload": ("causal self-attention forward, bf16, B8 S4096 H8 D64, BSHD "
+                                "contiguous, scale 1/8, N(0,1) inputs") if fwd_only else
+                               ("causal self-attention fwd+bwd, bf16, B4 S1024 H8 D64, BSHD "
+                                "contiguous, scale 1/8, N(0,1) inputs"),
+                   "batch": w.batch, "seq_len": w.seqlen_q, "heads": w.heads_q,
+                   "head_dim": w.head_dim, "mask": "causal", "flops_per_step": flops_step},
         "frac_of_peak": round(value / PEAK_TFLOPS["bf16"], 5),
         "roofline": roof,
         "kernels": kernels,
@@ -179,10 +190,23 @@ def main() -> int:
     if not args.no_extra:
         out["extra"] = extra(torch, S, synth, dev)
 
-    if not args.no_cpu:
+    if not args.no_cpu and not fwd_only:
         out["cpu_baseline"] = cpu_baseline(w, flops_step)
 
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def copy_calibration() -> int:
+    """A plain 1 GiB device-to-device copy, 5 times: its HBM counters read 1 GiB per
+    dispatch in each direction, which gives the scale of FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 1 << 30, "dispatches": 5}))
     return 0
 
 

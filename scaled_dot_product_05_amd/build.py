@@ -26,9 +26,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, tag + src + ".o")
+    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -39,20 +39,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
+    """Compile and link; ``defines`` (NAME=VALUE) select tile configurations."""
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if not defines else "_".join(d.replace("=", "") for d in defines) + "."
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, defines, tag), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -317,9 +317,12 @@ int64_t thd_items(int64_t total, int32_t batch, int tile) {
   return (total + tile - 1) / tile + batch;
 }
 
-size_t fwd_ws_bytes(const Shape& s) {
+int fwd_rows_per_tile(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kFwdBM : kFwdBM16; }
+
+size_t fwd_ws_bytes(const Shape& s, int32_t dtype) {
   if (!s.thd) return 0;
-  return size_t(round_up(thd_items(s.total_q, s.batch, kFwdBM) * int64_t(sizeof(WorkItem)), 256) + 256);
+  const int bm = fwd_rows_per_tile(dtype);
+  return size_t(round_up(thd_items(s.total_q, s.batch, bm) * int64_t(sizeof(WorkItem)), 256) + 256);
 }
 
 struct BwdWs {
@@ -367,11 +370,12 @@ int fwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
   Norm outs[2] = {no, nl};
   Norm ins[3] = {nq, nk, nv};
   if ((rc = check_outputs(outs, has_lse ? 2 : 1, ins, 3))) return rc;
-  size_t need = fwd_ws_bytes(a->s);
+  size_t need = fwd_ws_bytes(a->s, a->dtype);
   if (need && ws_bytes < need)
     return fail(SDPA_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
-  int64_t blocks = a->s.thd ? thd_items(a->s.total_q, a->s.batch, kFwdBM) * a->s.hq
-                            : int64_t((a->s.sq + kFwdBM - 1) / kFwdBM) * a->s.batch * a->s.hq;
+  const int bm = fwd_rows_per_tile(a->dtype);
+  int64_t blocks = a->s.thd ? thd_items(a->s.total_q, a->s.batch, bm) * a->s.hq
+                            : int64_t((a->s.sq + bm - 1) / bm) * a->s.batch * a->s.hq;
   if (blocks > INT32_MAX) return fail(SDPA_ERR_SHAPE, "problem too large for one launch");
   memset(p, 0, sizeof(*p));
   p->s = a->s;
@@ -580,7 +584,7 @@ int sdpa_fwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes) {
   int rc = check_desc(desc, &s);
   if (rc) return rc;
   if (!bytes) return fail(SDPA_ERR_NULL, "bytes is NULL");
-  *bytes = fwd_ws_bytes(s);
+  *bytes = fwd_ws_bytes(s, desc->dtype);
   return ok();
 }
 
@@ -600,7 +604,7 @@ int sdpa_fwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   FwdParams p;
   int rc = fwd_check(desc, q, k, v, o, lse, workspace_bytes, &a, &p);
   if (rc) return rc;
-  size_t need = fwd_ws_bytes(a.s);
+  size_t need = fwd_ws_bytes(a.s, a.dtype);
   if (need && !workspace) return fail(SDPA_ERR_WORKSPACE, "THD forward needs a workspace");
   debug_log("fwd", a, &p.aligned);
   if (a.s.batch == 0 || a.rows_q == 0) return ok();
@@ -608,11 +612,12 @@ int sdpa_fwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   hipError_t e;
   if (a.s.thd) {
     char* ws = static_cast<char*>(workspace);
-    int64_t nitems = thd_items(a.s.total_q, a.s.batch, kFwdBM);
+    const int bm = fwd_rows_per_tile(a.dtype);
+    int64_t nitems = thd_items(a.s.total_q, a.s.batch, bm);
     WorkItem* items = reinterpret_cast<WorkItem*>(ws);
     int32_t* count = reinterpret_cast<int32_t*>(ws + need - 256);
     SchedParams sp = sched_params(a.s, true, items, count);
-    sp.tile_own = kFwdBM;
+    sp.tile_own = bm;
     sp.tile_other = a.dtype == SDPA_DTYPE_F32 ? kFwdBN32 : kFwdBN16;
     sp.max_items = int32_t(nitems);
     if ((e = launch_schedule(sp, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");

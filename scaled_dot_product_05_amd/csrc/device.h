@@ -87,6 +87,16 @@ __device__ __forceinline__ uint16_t from_f32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + a.lo * b.lo + a.hi * b.hi for packed 16-bit pairs (v_dot2c_f32_{bf16,f16})
+template <bool BF>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  if constexpr (BF)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                           acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), acc, false);
+}
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 // 16 bytes from a row that is 16-byte aligned (al) or only element aligned.

@@ -21,6 +21,8 @@
 #include "launch.h"
 #include "profile.h"
 
+#include <type_traits>
+
 namespace sdpa {
 
 struct WorkPos {
@@ -51,18 +53,27 @@ __device__ __forceinline__ bool decode_work(const Shape& s, const WorkItem* work
 
 // ----------------------------------------------------------------------------------------
 // bf16 / fp16 inputs: MFMA 32x32x16, fp32 accumulation
+//
+// Each wave owns 32 query rows.  Key tiles are double-buffered in LDS: the global loads of
+// tile t+1 are in flight while tile t is computed, one barrier per tile.  Only tiles on the
+// window edges or past the end of the sequence evaluate the mask.  AL = every row start is
+// 16-byte aligned.
 // ----------------------------------------------------------------------------------------
-template <bool BF, int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
-  constexpr int BM = kFwdBM, BN = kFwdBN16;
+template <bool BF, int D, int BN, int MINB, bool AL>
+__global__ __launch_bounds__(kThreads, MINB) void fwd16_kernel(FwdParams p) {
+  constexpr int BM = 32 * kWaves;
   constexpr int KP = D + 8;   // K row pitch in elements (+16 B: conflict-free 16 B reads)
   constexpr int VP = BN + 8;  // V^T row pitch
+  constexpr int NG = BN / 8;  // 16-byte key groups per V^T row
   constexpr int NC = D / 16;  // contraction chunks of Q K^T
   constexpr int NKB = BN / 32;
   constexpr int NDB = D / 32;
   constexpr int NPC = BN / 16;  // contraction chunks of P V
   constexpr int LDC = BN * D / 8 / kThreads;  // 16-byte chunks per thread per tile
   static_assert(LDC >= 1 && LDC <= 4, "tile split");
+  // Lazy rescaling: the reference max only moves when a tile's max exceeds it by more than
+  // kTau (log2 units), so P <= 2^kTau and the O accumulator is rarely rescaled.
+  constexpr float kTau = 8.f;
   __shared__ __align__(16) uint16_t sk_[2][BN * KP];
   __shared__ __align__(16) uint16_t sv_[2][D * VP];
 
@@ -83,60 +94,79 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh +
                        g.krow0 * p.v.ss;
   uint16_t* ob = static_cast<uint16_t*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
-  const bool alq = p.aligned & kAlQ, alk = p.aligned & kAlK, alv = p.aligned & kAlV,
-             alo = p.aligned & kAlO;
 
+  // key tiles the workgroup visits [kt0, kt1), and those every one of its rows sees in full
   int j0, j1;
   key_range(s, g, q0, qend, j0, j1);
   const int kt0 = j0 / BN;
   const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  int kf0, kf1;
+  {
+    const int64_t lo_full = int64_t(qend - 1) + g.off + s.lo_rel;  // first key every row sees
+    const int64_t hi_full = min(int64_t(q0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
+    const int64_t a = lo_full <= 0 ? 0 : (lo_full + BN - 1) / BN;
+    const int64_t b = hi_full < 0 ? 0 : (hi_full + 1) / BN;
+    kf0 = int(clamp64(a, kt0, kt1));
+    kf1 = int(clamp64(b, kf0, kt1));
+  }
+  const int nf = kf1 - kf0;
 
   const int qw0 = q0 + wave * 32;
   const int qw1 = min(qw0 + 32, g.sq);
   const int qi = qw0 + l32;
-  const bool qvalid = qi < g.sq;
   int wj0 = 0, wj1 = 0;
   if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
 
+  // scores enter exp2 as fma(s, c, -m) with c = |scale| * log2(e) > 0; a negative scale
+  // is applied by negating q (exact).
+  const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
+  const uint32_t qsign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
   uint4 qf[NC];
+  {
+    const int qr = min(qi, g.sq - 1);
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    qf[c] = qvalid ? load16<2>(qb + qi * p.q.ss + 16 * c + 8 * hf, alq) : make_uint4(0, 0, 0, 0);
+    for (int cc = 0; cc < NC; ++cc) {
+      uint4 t = load16<2>(qb + qr * p.q.ss + 16 * cc + 8 * hf, AL);
+      qf[cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
+    }
+  }
 
   f32x16_t acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
   float m_run = kNegInf, l_run = 0.f;
 
+  // ---- global -> LDS staging ----
   uint4 kst[LDC], vst[LDC];
   const int vdc = tid % (D / 8), vkg = tid / (D / 8);
-  auto gload = [&](int kt) {
-    const int base = kt * BN;
+  const int jlast = g.sk - 1;
+  auto loadK = [&](int t) {
 #pragma unroll
     for (int u = 0; u < LDC; ++u) {
-      int ci = tid + u * kThreads;
-      int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      int j = base + row;
-      kst[u] = j < g.sk ? load16<2>(kb + j * p.k.ss + col, alk) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int x = 0; x < LDC; ++x) {
-      int j = base + vkg * LDC + x;
-      vst[x] = j < g.sk ? load16<2>(vb + j * p.v.ss + vdc * 8, alv) : make_uint4(0, 0, 0, 0);
+      const int ci = tid + u * kThreads;
+      kst[u] = load16<2>(kb + int64_t(min(t * BN + ci / (D / 8), jlast)) * p.k.ss + (ci % (D / 8)) * 8, AL);
     }
   };
-  auto sstore = [&](int buf) {
+  auto loadV = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < LDC; ++u)
+      vst[u] = load16<2>(vb + int64_t(min(t * BN + vkg * LDC + u, jlast)) * p.v.ss + vdc * 8, AL);
+  };
+  auto storeK = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < LDC; ++u) {
-      int ci = tid + u * kThreads;
-      int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&sk_[buf][row * KP + col]) = kst[u];
+      const int ci = tid + u * kThreads;
+      *reinterpret_cast<uint4*>(&sk_[buf][(ci / (D / 8)) * KP + (ci % (D / 8)) * 8]) = kst[u];
     }
-    // V^T: this thread's LDC keys x 8 d, written as 8 rows of LDC contiguous keys
-    const int pos = tpos(vkg * LDC);
+  };
+  // V^T rows d = vdc*8 + e hold keys in transposed order (tpos) with the 16-byte key groups
+  // XOR-swizzled by d/8, so the 8 lanes writing rows 8 apart hit different banks.
+  const int vpos = tpos(vkg * LDC);
+  const int vcol = (((vpos >> 3) ^ (vdc & (NG - 1))) << 3) | (vpos & 7);
+  auto storeV = [&](int buf) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = &sv_[buf][(vdc * 8 + e) * VP + pos];
+      uint16_t* dst = &sv_[buf][(vdc * 8 + e) * VP + vcol];
       if constexpr (LDC == 4) {
         uint32_t lo = elem16(vst[0], e) | (elem16(vst[1], e) << 16);
         uint32_t hi = elem16(vst[2], e) | (elem16(vst[3], e) << 16);
@@ -148,81 +178,122 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
       }
     }
   };
+  int voff[NDB][NPC];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int cc = 0; cc < NPC; ++cc) {
+      const int d = db * 32 + l32;
+      voff[db][cc] = d * VP + (((2 * cc + hf) ^ ((d >> 3) & (NG - 1))) << 3);
+    }
+  const int koff = l32 * KP + 8 * hf;
 
-  if (kt0 < kt1) {
-    gload(kt0);
-    sstore(0);
-  }
-  __syncthreads();
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) gload(kt + 1);
-    const int kbase = kt * BN;
-    if (kbase < wj1 && kbase + BN > wj0) {
-      f32x16_t st[NKB];
+  // ---- building blocks ----
+  auto scores = [&](int buf, f32x16_t (&st)[NKB]) {
 #pragma unroll
-      for (int k2 = 0; k2 < NKB; ++k2) {
-        st[k2] = zero16();
+    for (int k2 = 0; k2 < NKB; ++k2) {
+      st[k2] = zero16();
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          uint4 a = *reinterpret_cast<const uint4*>(&sk_[buf][(k2 * 32 + l32) * KP + 16 * c + 8 * hf]);
-          st[k2] = mfma16<BF>(a, qf[c], st[k2]);
-        }
-      }
-      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
-      float mx = kNegInf;
-#pragma unroll
-      for (int k2 = 0; k2 < NKB; ++k2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = st[k2][r] * s.scale_log2;
-          if (!full) {
-            int j = kbase + k2 * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (!visible(s, g, qi, j)) x = kNegInf;
-          }
-          st[k2][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float ps = 0.f;
-      uint4 pf[NPC];
-#pragma unroll
-      for (int c = 0; c < NPC; ++c) {
-        const int k2 = c >> 1, rb = (c & 1) * 8;
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = fast_exp2(st[k2][rb + j] - m_use);
-          ps += e[j];
-        }
-        pf[c] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
-                           pack2<BF>(e[6], e[7]));
-      }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-#pragma unroll
-        for (int c = 0; c < NPC; ++c) {
-          uint4 a = *reinterpret_cast<const uint4*>(&sv_[buf][(db * 32 + l32) * VP + 16 * c + 8 * hf]);
-          acc[db] = mfma16<BF>(a, pf[c], acc[db]);
-        }
+      for (int cc = 0; cc < NC; ++cc) {
+        uint4 a = *reinterpret_cast<const uint4*>(&sk_[buf][koff + k2 * 32 * KP + 16 * cc]);
+        st[k2] = mfma16<BF>(a, qf[cc], st[k2]);
       }
     }
-    if (more) sstore(buf ^ 1);
+  };
+  auto pv = [&](int buf, const uint4 (&pf)[NPC]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < NPC; ++cc) {
+        uint4 a = *reinterpret_cast<const uint4*>(&sv_[buf][voff[db][cc]]);
+        acc[db] = mfma16<BF>(a, pf[cc], acc[db]);
+      }
+  };
+  // Row max of a score tile against the reference; returns true when some lane's reference
+  // has to move (then the caller settles pending P V work before rescale()).
+  auto tile_max = [&](const f32x16_t (&st)[NKB], float& m_tile) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[k2][r]);
+    mx = fmaxf(mx, xor32(mx));
+    m_tile = mx == kNegInf ? kNegInf : mx * c;
+    return __builtin_amdgcn_ballot_w64(m_tile > m_run + kTau) != 0;
+  };
+  auto rescale = [&](float m_tile) {
+    const bool raise = m_tile > m_run + kTau;
+    const float alpha = raise ? fast_exp2(m_run - m_tile) : 1.f;
+    m_run = raise ? m_tile : m_run;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+  };
+  auto probs = [&](const f32x16_t (&st)[NKB], uint4 (&pf)[NPC]) {
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NPC; ++cc) {
+      const int k2 = cc >> 1, rb = (cc & 1) * 8;
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = fast_exp2(__builtin_fmaf(st[k2][rb + j], c, -m_use));
+      ps0 += (e[0] + e[1]) + (e[2] + e[3]);
+      ps1 += (e[4] + e[5]) + (e[6] + e[7]);
+      pf[cc] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
+                          pack2<BF>(e[6], e[7]));
+    }
+    l_run += ps0 + ps1;
+  };
+
+  // ---- key tiles kt0 .. kt1-1, double-buffered: tile t+1 is loaded while t is computed ----
+  if (kt0 < kt1) {
+    loadK(kt0);
+    loadV(kt0);
+    storeK(0);
+    storeV(0);
+  }
+  __syncthreads();
+  for (int t = kt0; t < kt1; ++t) {
+    const int buf = (t - kt0) & 1;
+    const bool more = t + 1 < kt1;
+    if (more) {
+      loadK(t + 1);
+      loadV(t + 1);
+    }
+    const int kbase = t * BN;
+    if (kbase < wj1 && kbase + BN > wj0) {  // this wave sees part of the tile
+      f32x16_t st[NKB];
+      scores(buf, st);
+      if (!(t >= kf0 && t < kf1) && !tile_full(s, g, qw0, qw1, kbase, kbase + BN)) {
+        // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
+        const int base_rel = kbase - qi - g.off + 4 * hf;
+        const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+#pragma unroll
+        for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
+            st[k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[k2][r] : kNegInf;
+          }
+      }
+      float m_tile;
+      if (tile_max(st, m_tile)) rescale(m_tile);
+      uint4 pf[NPC];
+      probs(st, pf);
+      pv(buf, pf);
+    }
+    if (more) {
+      storeK(buf ^ 1);
+      storeV(buf ^ 1);
+    }
     __syncthreads();
   }
 
   const float lt = l_run + xor32(l_run);
-  if (qvalid) {
+  if (qi < g.sq) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* orow = ob + qi * p.o.ss;
 #pragma unroll
@@ -232,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
         int d = db * 32 + 8 * gq + 4 * hf;
         uint32_t lo = pack2<BF>(acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv);
         uint32_t hi = pack2<BF>(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv);
-        store8(orow + d, lo, hi, alo);
+        store8(orow + d, lo, hi, AL);
       }
     }
     if (hf == 0 && p.lse.ptr) {
@@ -446,27 +517,39 @@ static hipError_t go(K kernel, int blocks, hipStream_t st, const FwdParams& p) {
   return hipGetLastError();
 }
 
+template <bool BF, int D, int BN, int MINB>
+static hipError_t go16(const FwdParams& p, hipStream_t st) {
+  const Shape& s = p.s;
+  constexpr int BM = 32 * kWaves;
+  static_assert(BM == kFwdBM16, "host and kernel tile rows differ");
+  int64_t blocks = s.thd ? (s.total_q + BM - 1) / BM + s.batch : int64_t((s.sq + BM - 1) / BM) * s.batch;
+  blocks *= s.hq;
+  if (blocks <= 0) return hipSuccess;
+  const bool al = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
+  return al ? go(fwd16_kernel<BF, D, BN, MINB, true>, int(blocks), st, p)
+            : go(fwd16_kernel<BF, D, BN, MINB, false>, int(blocks), st, p);
+}
+
+template <bool BF>
+static hipError_t fwd16_dispatch(const FwdParams& p, hipStream_t st) {
+  switch (p.s.d) {
+    case 32: return go16<BF, 32, 64, 2>(p, st);
+    case 64: return go16<BF, 64, kFwdBN16_D64, kFwdMinB_D64>(p, st);
+    default: return go16<BF, 128, kFwdBN16_D128, kFwdMinB_D128>(p, st);
+  }
+}
+
 hipError_t launch_fwd(const FwdParams& p, DType dt, hipStream_t st) {
   const Shape& s = p.s;
+  if (dt == DType::BF16) return fwd16_dispatch<true>(p, st);
+  if (dt == DType::F16) return fwd16_dispatch<false>(p, st);
   int64_t blocks = s.thd ? (s.total_q + kFwdBM - 1) / kFwdBM + s.batch
                          : int64_t((s.sq + kFwdBM - 1) / kFwdBM) * s.batch;
   blocks *= s.hq;
   if (blocks <= 0) return hipSuccess;
-  int nb = int(blocks);
-  switch (dt) {
-    case DType::BF16:
-      if (s.d == 32) return go(fwd16_kernel<true, 32>, nb, st, p);
-      if (s.d == 64) return go(fwd16_kernel<true, 64>, nb, st, p);
-      return go(fwd16_kernel<true, 128>, nb, st, p);
-    case DType::F16:
-      if (s.d == 32) return go(fwd16_kernel<false, 32>, nb, st, p);
-      if (s.d == 64) return go(fwd16_kernel<false, 64>, nb, st, p);
-      return go(fwd16_kernel<false, 128>, nb, st, p);
-    default:
-      if (s.d == 32) return go(fwd32_kernel<32>, nb, st, p);
-      if (s.d == 64) return go(fwd32_kernel<64>, nb, st, p);
-      return go(fwd32_kernel<128>, nb, st, p);
-  }
+  if (s.d == 32) return go(fwd32_kernel<32>, int(blocks), st, p);
+  if (s.d == 64) return go(fwd32_kernel<64>, int(blocks), st, p);
+  return go(fwd32_kernel<128>, int(blocks), st, p);
 }
 
 }  // namespace sdpa

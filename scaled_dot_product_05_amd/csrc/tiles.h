@@ -6,9 +6,26 @@ namespace sdpa {
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = 64 * kWaves;  // threads per workgroup
 
-// forward: one workgroup owns kFwdBM query rows (32 per wave) of one (batch, q head)
-constexpr int kFwdBM = 128;
-constexpr int kFwdBN16 = 64;  // keys per K/V tile, 16-bit inputs
+// forward: one workgroup owns the query rows of its waves (32 per wave) of one (batch, q head)
+constexpr int kFwdBM = 128;  // fp32
+#ifndef SDPA_FWD_BN_D64
+#define SDPA_FWD_BN_D64 64
+#endif
+#ifndef SDPA_FWD_MINB_D64
+#define SDPA_FWD_MINB_D64 2
+#endif
+#ifndef SDPA_FWD_BN_D128
+#define SDPA_FWD_BN_D128 64
+#endif
+#ifndef SDPA_FWD_MINB_D128
+#define SDPA_FWD_MINB_D128 2
+#endif
+constexpr int kFwdBM16 = 32 * kWaves;
+constexpr int kFwdBN16 = 64;         // keys per K/V tile, 16-bit inputs, head_dim 32
+constexpr int kFwdBN16_D64 = SDPA_FWD_BN_D64;    // keys per tile and minimum workgroups
+constexpr int kFwdMinB_D64 = SDPA_FWD_MINB_D64;  // per CU, head_dim 64
+constexpr int kFwdBN16_D128 = SDPA_FWD_BN_D128;
+constexpr int kFwdMinB_D128 = SDPA_FWD_MINB_D128;
 constexpr int kFwdBN32 = 32;  // keys per K/V tile, fp32 inputs
 
 // backward dQ: one workgroup owns kBwdQ query rows (32 per wave); keys stream in kBwdQInner tiles
