@@ -329,18 +329,21 @@ struct BwdWs {
   int64_t delta_off, wq_off, cq_off, wk_off, ck_off, total;
 };
 
-BwdWs bwd_ws_layout(const Shape& s) {
+int bwd_q_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdQ32 : kBwdQ16; }
+int bwd_k_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdK32 : kBwdK16; }
+
+BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
   BwdWs w{};
   int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
   w.delta_off = 0;
   int64_t off = round_up(rows * 4, 256);
   if (s.thd) {
     w.wq_off = off;
-    off = round_up(off + thd_items(s.total_q, s.batch, kBwdQ) * int64_t(sizeof(WorkItem)), 256);
+    off = round_up(off + thd_items(s.total_q, s.batch, bwd_q_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
     w.cq_off = off;
     off += 256;
     w.wk_off = off;
-    off = round_up(off + thd_items(s.total_k, s.batch, kBwdK) * int64_t(sizeof(WorkItem)), 256);
+    off = round_up(off + thd_items(s.total_k, s.batch, bwd_k_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
     w.ck_off = off;
     off += 256;
   }
@@ -415,7 +418,7 @@ int bwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
   Norm outs[3] = {ndq, ndk, ndv};
   Norm ins[7] = {nq, nk, nv, no, ndo, nl, ndl};
   if ((rc = check_outputs(outs, 3, ins, has_dlse ? 7 : 6))) return rc;
-  BwdWs w = bwd_ws_layout(a->s);
+  BwdWs w = bwd_ws_layout(a->s, a->dtype);
   if (ws_bytes < size_t(w.total))
     return fail(SDPA_ERR_WORKSPACE, "workspace %zu bytes, %lld needed", ws_bytes, (long long)w.total);
   memset(p, 0, sizeof(*p));
@@ -633,7 +636,7 @@ int sdpa_bwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes) {
   int rc = check_desc(desc, &s);
   if (rc) return rc;
   if (!bytes) return fail(SDPA_ERR_NULL, "bytes is NULL");
-  *bytes = size_t(bwd_ws_layout(s).total);
+  *bytes = size_t(bwd_ws_layout(s, desc->dtype).total);
   return ok();
 }
 
@@ -658,7 +661,7 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   int rc = bwd_check(desc, q, k, v, o, lse, dout, dlse, dq, dk, dv, workspace_bytes, &a, &p);
   if (rc) return rc;
   if (accumulate != 0 && accumulate != 1) return fail(SDPA_ERR_ARG, "accumulate must be 0 or 1");
-  BwdWs w = bwd_ws_layout(a.s);
+  BwdWs w = bwd_ws_layout(a.s, a.dtype);
   if (w.total > 0 && !workspace) return fail(SDPA_ERR_WORKSPACE, "backward needs a workspace");
   debug_log("bwd", a, &p.aligned);
   if (a.s.batch == 0 || (a.rows_q == 0 && a.rows_k == 0)) return ok();
@@ -670,14 +673,15 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   if (a.s.thd) {
     SchedParams sq = sched_params(a.s, true, reinterpret_cast<WorkItem*>(ws + w.wq_off),
                                   reinterpret_cast<int32_t*>(ws + w.cq_off));
-    sq.tile_own = kBwdQ;
-    sq.tile_other = kBwdQInner;
-    sq.max_items = int32_t(thd_items(a.s.total_q, a.s.batch, kBwdQ));
+    const bool f32 = a.dtype == SDPA_DTYPE_F32;
+    sq.tile_own = bwd_q_rows(a.dtype);
+    sq.tile_other = f32 ? 32 : kBwdQInner;
+    sq.max_items = int32_t(thd_items(a.s.total_q, a.s.batch, sq.tile_own));
     SchedParams sk = sched_params(a.s, false, reinterpret_cast<WorkItem*>(ws + w.wk_off),
                                   reinterpret_cast<int32_t*>(ws + w.ck_off));
-    sk.tile_own = kBwdK;
-    sk.tile_other = kBwdKInner;
-    sk.max_items = int32_t(thd_items(a.s.total_k, a.s.batch, kBwdK));
+    sk.tile_own = bwd_k_rows(a.dtype);
+    sk.tile_other = f32 ? 32 : kBwdKInner;
+    sk.max_items = int32_t(thd_items(a.s.total_k, a.s.batch, sk.tile_own));
     if ((e = launch_schedule(sq, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
     if ((e = launch_schedule(sk, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
     p.work_q = sq.items;

@@ -7,12 +7,15 @@
 //   dS_ij = P_ij (dP_ij - Delta_i),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
 // Three launches on one stream, no atomics anywhere:
 //   pre   Delta for every query row (streaming, HBM bound);
-//   dq    one workgroup per 128 query rows of a q head, streaming the key tiles;
-//   dkdv  one workgroup per 128 keys of a kv head, streaming the query tiles of every q
-//         head of its group, so dK and dV of a GQA group are summed in registers.
+//   dq    one workgroup per 64 (16-bit) or 128 (fp32) query rows of a q head, streaming
+//         the key tiles;
+//   dkdv  one workgroup per 64 (16-bit) or 128 (fp32) keys of a kv head, streaming the
+//         query tiles of every q head of its group, so dK and dV of a GQA group are summed
+//         in registers.
 // In 16-bit mode the operands that must be contracted over rows (K in dq; Q and dO in
 // dkdv) are also kept transposed in LDS, written once per tile from the same registers
-// that fill the row-major copy.  fp32 mode uses true fp32 MFMA and reads the transposed
+// that fill the row-major copy.  16-bit workgroups own 64 rows and split the streamed tile
+// between wave pairs, so small problems still launch enough waves.  fp32 mode uses true fp32 MFMA and reads the transposed
 // operand element-wise from the row-major tile.
 #include "device.h"
 #include "launch.h"
@@ -111,12 +114,14 @@ struct Tile16 {
   static constexpr int TP = ROWS + 8;                  // transposed pitch (elements)
   static_assert(RPT >= 1 && RPT <= 4, "tile split");
   uint4 r[RPT];
+  // Rows past nrows read the last row instead (in bounds, branch-free); callers give them
+  // P = 0.  nrows >= 1.
   __device__ __forceinline__ void load(const uint16_t* base, int64_t ss, int row0, int nrows, bool al) {
     const int dc = threadIdx.x % (D / 8), rg = threadIdx.x / (D / 8);
 #pragma unroll
     for (int x = 0; x < RPT; ++x) {
-      int row = row0 + rg * RPT + x;
-      r[x] = row < nrows ? load16<2>(base + row * ss + dc * 8, al) : make_uint4(0, 0, 0, 0);
+      const int row = min(row0 + rg * RPT + x, nrows - 1);
+      r[x] = load16<2>(base + int64_t(row) * ss + dc * 8, al);
     }
   }
   __device__ __forceinline__ void store_rows(uint16_t* lds) const {
@@ -165,17 +170,22 @@ __device__ __forceinline__ void out4_32(float* p, const float* v, float scale, b
 }
 
 // ----------------------------------------------------------------------------------------
-// dQ, 16-bit
+// dQ, 16-bit.  A workgroup owns 64 query rows of one q head and streams 64-key tiles.
+// Wave w takes query block w&1 (32 rows) and key half w>>1 of every tile; the two key
+// halves' partial dQ are summed once through LDS at the end (fixed order, no atomics).
 // ----------------------------------------------------------------------------------------
 template <bool BF, int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq16_kernel(BwdParams p) {
-  constexpr int BM = kBwdQ, BN = kBwdQInner;
+  constexpr int BM = kBwdQ16, BN = kBwdQInner;
   using T = Tile16<D>;
-  static_assert(BN == T::ROWS, "inner tile");
-  constexpr int NC = D / 16, NKB = BN / 32, NDB = D / 32, NPC = BN / 16;
-  __shared__ __align__(16) uint16_t sk_[BN * T::RP];
-  __shared__ __align__(16) uint16_t skt_[D * T::TP];
-  __shared__ __align__(16) uint16_t sv_[BN * T::RP];
+  static_assert(BN == T::ROWS && BM == 64, "tile split");
+  constexpr int NC = D / 16, NDB = D / 32;
+  constexpr int OFF_KT = BN * T::RP, OFF_V = OFF_KT + D * T::TP, SMEM = OFF_V + BN * T::RP;
+  static_assert(2 * NDB * 16 * 64 * 4 <= SMEM * 2, "reduction buffer");
+  __shared__ __align__(16) uint16_t smem[SMEM];
+  uint16_t* sk_ = smem;
+  uint16_t* skt_ = smem + OFF_KT;
+  uint16_t* sv_ = smem + OFF_V;
 
   const Shape& s = p.s;
   BwdPos w;
@@ -185,6 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq16_kernel(BwdParams p) {
   if (q0 >= g.sq) return;
   const int qend = min(q0 + BM, g.sq);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int qblk = wave & 1, khalf = wave >> 1;
   const int hk = w.h / s.group;
   const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh + g.qrow0 * p.q.ss;
   const uint16_t* gb = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + w.h * p.dout.sh +
@@ -196,17 +207,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq16_kernel(BwdParams p) {
   int j0, j1;
   key_range(s, g, q0, qend, j0, j1);
   const int kt0 = j0 / BN, kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
-  const int qw0 = q0 + wave * 32, qw1 = min(qw0 + 32, g.sq);
+  const int qw0 = q0 + qblk * 32, qw1 = min(qw0 + 32, g.sq);
   const int qi = qw0 + l32;
   const bool qvalid = qi < g.sq;
   int wj0 = 0, wj1 = 0;
   if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
 
   uint4 qf[NC], gf[NC];
+  {
+    const int qr = min(qi, g.sq - 1);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    qf[c] = qvalid ? load16<2>(qb + qi * p.q.ss + 16 * c + 8 * hf, p.aligned & kAlQ) : make_uint4(0, 0, 0, 0);
-    gf[c] = qvalid ? load16<2>(gb + qi * p.dout.ss + 16 * c + 8 * hf, p.aligned & kAlDO) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = load16<2>(qb + qr * p.q.ss + 16 * c + 8 * hf, p.aligned & kAlQ);
+      gf[c] = load16<2>(gb + qr * p.dout.ss + 16 * c + 8 * hf, p.aligned & kAlDO);
+    }
   }
   float lse2 = __builtin_inff(), dl = 0.f;
   if (qvalid) {
@@ -219,80 +233,99 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq16_kernel(BwdParams p) {
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
   T kt, vt;
+  if (kt0 < kt1) {
+    kt.load(kb, p.k.ss, kt0 * BN, g.sk, p.aligned & kAlK);
+    vt.load(vb, p.v.ss, kt0 * BN, g.sk, p.aligned & kAlV);
+  }
   for (int t = kt0; t < kt1; ++t) {
     const int kbase = t * BN;
-    kt.load(kb, p.k.ss, kbase, g.sk, p.aligned & kAlK);
-    vt.load(vb, p.v.ss, kbase, g.sk, p.aligned & kAlV);
     __syncthreads();  // previous tile fully consumed
     kt.store_rows(sk_);
     kt.store_transposed(skt_);
     vt.store_rows(sv_);
     __syncthreads();
-    if (kbase < wj1 && kbase + BN > wj0) {
-      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
-      uint4 dsf[NPC];
+    if (t + 1 < kt1) {  // next tile's global loads overlap this tile's compute
+      kt.load(kb, p.k.ss, kbase + BN, g.sk, p.aligned & kAlK);
+      vt.load(vb, p.v.ss, kbase + BN, g.sk, p.aligned & kAlV);
+    }
+    const int kw = kbase + 32 * khalf;  // this wave's 32 keys
+    if (kw < wj1 && kw + 32 > wj0) {
+      const bool full = tile_full(s, g, qw0, qw1, kw, kw + 32);
+      f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
-      for (int k2 = 0; k2 < NKB; ++k2) {
-        f32x16_t st = zero16(), dp = zero16();
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          uint4 a = *reinterpret_cast<const uint4*>(&sk_[(k2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
-          st = mfma16<BF>(a, qf[c], st);
-          uint4 bv = *reinterpret_cast<const uint4*>(&sv_[(k2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
-          dp = mfma16<BF>(bv, gf[c], dp);
-        }
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(st[r] * s.scale_log2 - lse2);
-          if (!full) {
-            int j = kbase + k2 * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (!visible(s, g, qi, j)) pr = 0.f;
-          }
-          ds[r] = pr * (dp[r] - dl);
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          dsf[2 * k2 + h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
-                                        pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
+      for (int c = 0; c < NC; ++c) {
+        uint4 a = *reinterpret_cast<const uint4*>(&sk_[(32 * khalf + l32) * T::RP + 16 * c + 8 * hf]);
+        uint4 bv = *reinterpret_cast<const uint4*>(&sv_[(32 * khalf + l32) * T::RP + 16 * c + 8 * hf]);
+        st = mfma16<BF>(a, qf[c], st);
+        dp = mfma16<BF>(bv, gf[c], dp);
       }
+      float ds[16];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(st[r] * s.scale_log2 - lse2);
+        if (!full && !visible(s, g, qi, kw + 8 * (r >> 2) + 4 * hf + (r & 3))) pr = 0.f;
+        ds[r] = pr * (dp[r] - dl);
+      }
+      uint4 dsf[2];
 #pragma unroll
-        for (int c = 0; c < NPC; ++c) {
-          uint4 a = *reinterpret_cast<const uint4*>(&skt_[(db * 32 + l32) * T::TP + 16 * c + 8 * hf]);
+      for (int h2 = 0; h2 < 2; ++h2)
+        dsf[h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                             pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          uint4 a = *reinterpret_cast<const uint4*>(&skt_[(db * 32 + l32) * T::TP + 32 * khalf + 16 * c + 8 * hf]);
           acc[db] = mfma16<BF>(a, dsf[c], acc[db]);
         }
-      }
     }
   }
-  if (qvalid) {
+  // sum the two key halves: khalf 1 parks its partial in LDS, khalf 0 adds and writes
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  if (khalf == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((qblk * NDB + db) * 16 + r) * 64 + lane] = acc[db][r];
+  }
+  __syncthreads();
+  if (khalf == 0 && qvalid) {
     uint16_t* row = dqb + qi * p.dq.ss;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        float v[4] = {acc[db][4 * gq], acc[db][4 * gq + 1], acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = acc[db][4 * gq + e] + red[((qblk * NDB + db) * 16 + 4 * gq + e) * 64 + lane];
         out4_16<BF>(row + db * 32 + 8 * gq + 4 * hf, v, s.scale, p.aligned & kAlDQ, p.accumulate);
       }
   }
 }
 
 // ----------------------------------------------------------------------------------------
-// dK, dV, 16-bit
+// dK, dV, 16-bit.  A workgroup owns 64 keys of one kv head and streams 64-row query tiles
+// of every q head of the group.  Wave w takes key block w&1 (32 keys) and query half w>>1
+// of every tile; the two query halves' partial dK, dV are summed once through LDS.
 // ----------------------------------------------------------------------------------------
 template <bool BF, int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv16_kernel(BwdParams p) {
-  constexpr int BK = kBwdK, BQ = kBwdKInner;
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void bwd_dkdv16_kernel(BwdParams p) {
+  constexpr int BK = kBwdK16, BQ = kBwdKInner;
   using T = Tile16<D>;
-  static_assert(BQ == T::ROWS, "inner tile");
-  constexpr int NC = D / 16, NQB = BQ / 32, NDB = D / 32, NQC = BQ / 16;
-  __shared__ __align__(16) uint16_t sq_[BQ * T::RP];
-  __shared__ __align__(16) uint16_t sqt_[D * T::TP];
-  __shared__ __align__(16) uint16_t sg_[BQ * T::RP];
-  __shared__ __align__(16) uint16_t sgt_[D * T::TP];
+  static_assert(BQ == T::ROWS && BK == 64, "tile split");
+  constexpr int NC = D / 16, NDB = D / 32;
+  constexpr int OFF_QT = BQ * T::RP, OFF_G = OFF_QT + D * T::TP, OFF_GT = OFF_G + BQ * T::RP;
+  constexpr int SMEM = OFF_GT + D * T::TP;
+  static_assert(2 * 2 * NDB * 16 * 64 * 4 <= SMEM * 2, "reduction buffer");
+  __shared__ __align__(16) uint16_t smem[SMEM];
   __shared__ __align__(16) float slse_[BQ];
   __shared__ __align__(16) float sdl_[BQ];
+  uint16_t* sq_ = smem;
+  uint16_t* sqt_ = smem + OFF_QT;
+  uint16_t* sg_ = smem + OFF_G;
+  uint16_t* sgt_ = smem + OFF_GT;
 
   const Shape& s = p.s;
   BwdPos w;
@@ -302,6 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv16_kernel(BwdParams p) {
   if (k0 >= g.sk) return;
   const int kend = min(k0 + BK, g.sk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int kblk = wave & 1, qhalf = wave >> 1;
   const int hk = w.h;
   const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
   const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
@@ -311,17 +345,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv16_kernel(BwdParams p) {
   int i0, i1;
   query_range(s, g, k0, kend, i0, i1);
   const int qt0 = i0 / BQ, qt1 = i1 > i0 ? (i1 + BQ - 1) / BQ : qt0;
-  const int kw0 = k0 + wave * 32, kw1 = min(kw0 + 32, g.sk);
+  const int kw0 = k0 + kblk * 32, kw1 = min(kw0 + 32, g.sk);
   const int kj = kw0 + l32;
   const bool kvalid = kj < g.sk;
   int wi0 = 0, wi1 = 0;
   if (kw0 < kw1) query_range(s, g, kw0, kw1, wi0, wi1);
 
   uint4 kf[NC], vf[NC];
+  {
+    const int kr = min(kj, g.sk - 1);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    kf[c] = kvalid ? load16<2>(kb + kj * p.k.ss + 16 * c + 8 * hf, p.aligned & kAlK) : make_uint4(0, 0, 0, 0);
-    vf[c] = kvalid ? load16<2>(vb + kj * p.v.ss + 16 * c + 8 * hf, p.aligned & kAlV) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = load16<2>(kb + kr * p.k.ss + 16 * c + 8 * hf, p.aligned & kAlK);
+      vf[c] = load16<2>(vb + kr * p.v.ss + 16 * c + 8 * hf, p.aligned & kAlV);
+    }
   }
   f32x16_t adk[NDB], adv[NDB];
 #pragma unroll
@@ -330,86 +367,99 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv16_kernel(BwdParams p) {
     adv[i] = zero16();
   }
 
+  // items = (q head of the group, q tile); the next item's global loads overlap compute
   T qt, gt;
-  for (int gi = 0; gi < s.group; ++gi) {
-    const int h = hk * s.group + gi;
-    const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss;
-    const uint16_t* gb = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh +
-                         g.qrow0 * p.dout.ss;
-    for (int t = qt0; t < qt1; ++t) {
-      const int qbase = t * BQ;
-      qt.load(qb, p.q.ss, qbase, g.sq, p.aligned & kAlQ);
-      gt.load(gb, p.dout.ss, qbase, g.sq, p.aligned & kAlDO);
-      float lv = __builtin_inff(), dv = 0.f;
-      if (tid < BQ) {
-        int i = qbase + tid;
-        if (i < g.sq) {
-          float l = p.lse.ptr[w.b * p.lse.sb + h * p.lse.sh + (g.qrow0 + i) * p.lse.ss];
-          lv = l == kNegInf ? __builtin_inff() : l * kLog2e;
-          dv = p.delta[delta_index(s, w.b, h, g, i)];
+  const int nq = qt1 - qt0, nitems = s.group * nq;
+  float lv = __builtin_inff(), dv = 0.f;
+  auto load_item = [&](int it) {
+    const int h = hk * s.group + it / nq, qbase = (qt0 + it % nq) * BQ;
+    qt.load(static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss,
+            p.q.ss, qbase, g.sq, p.aligned & kAlQ);
+    gt.load(static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh + g.qrow0 * p.dout.ss,
+            p.dout.ss, qbase, g.sq, p.aligned & kAlDO);
+    if (tid < BQ) {
+      const int i = qbase + tid, ic = min(i, g.sq - 1);
+      const float l = p.lse.ptr[w.b * p.lse.sb + h * p.lse.sh + (g.qrow0 + ic) * p.lse.ss];
+      const float d = p.delta[delta_index(s, w.b, h, g, ic)];
+      lv = (i < g.sq && l != kNegInf) ? l * kLog2e : __builtin_inff();
+      dv = i < g.sq ? d : 0.f;
+    }
+  };
+  if (nitems > 0) load_item(0);
+  for (int it = 0; it < nitems; ++it) {
+    const int qbase = (qt0 + it % nq) * BQ;
+    __syncthreads();
+    qt.store_rows(sq_);
+    qt.store_transposed(sqt_);
+    gt.store_rows(sg_);
+    gt.store_transposed(sgt_);
+    if (tid < BQ) {
+      slse_[tid] = lv;
+      sdl_[tid] = dv;
+    }
+    __syncthreads();
+    if (it + 1 < nitems) load_item(it + 1);
+    const int qr0 = qbase + 32 * qhalf;  // this wave's 32 query rows
+    if (qr0 < wi1 && qr0 + 32 > wi0) {
+      const bool full = tile_full(s, g, qr0, min(qr0 + 32, g.sq), kw0, kw1);
+      f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 a = *reinterpret_cast<const uint4*>(&sq_[(32 * qhalf + l32) * T::RP + 16 * c + 8 * hf]);
+        uint4 b2 = *reinterpret_cast<const uint4*>(&sg_[(32 * qhalf + l32) * T::RP + 16 * c + 8 * hf]);
+        st = mfma16<BF>(a, kf[c], st);
+        dp = mfma16<BF>(b2, vf[c], dp);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ql = 32 * qhalf + 8 * g4 + 4 * hf;
+        float4 l4 = *reinterpret_cast<const float4*>(&slse_[ql]);
+        float4 d4 = *reinterpret_cast<const float4*>(&sdl_[ql]);
+        float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float x = fast_exp2(st[r] * s.scale_log2 - la[e]);
+          if (!full && !visible(s, g, qbase + ql + e, kj)) x = 0.f;
+          pr[r] = x;
+          ds[r] = x * (dp[r] - da[e]);
         }
       }
-      __syncthreads();
-      qt.store_rows(sq_);
-      qt.store_transposed(sqt_);
-      gt.store_rows(sg_);
-      gt.store_transposed(sgt_);
-      if (tid < BQ) {
-        slse_[tid] = lv;
-        sdl_[tid] = dv;
+      uint4 pf[2], dsf[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        pf[h2] = make_uint4(pack2<BF>(pr[8 * h2], pr[8 * h2 + 1]), pack2<BF>(pr[8 * h2 + 2], pr[8 * h2 + 3]),
+                            pack2<BF>(pr[8 * h2 + 4], pr[8 * h2 + 5]), pack2<BF>(pr[8 * h2 + 6], pr[8 * h2 + 7]));
+        dsf[h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                             pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
       }
-      __syncthreads();
-      if (qbase < wi1 && qbase + BQ > wi0) {
-        const bool full = tile_full(s, g, qbase, min(qbase + BQ, g.sq), kw0, kw1);
-        uint4 pf[NQC], dsf[NQC];
 #pragma unroll
-        for (int qb2 = 0; qb2 < NQB; ++qb2) {
-          f32x16_t st = zero16(), dp = zero16();
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            uint4 a = *reinterpret_cast<const uint4*>(&sq_[(qb2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
-            st = mfma16<BF>(a, kf[c], st);
-            uint4 b2 = *reinterpret_cast<const uint4*>(&sg_[(qb2 * 32 + l32) * T::RP + 16 * c + 8 * hf]);
-            dp = mfma16<BF>(b2, vf[c], dp);
-          }
-          float pr[16], ds[16];
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int ql = qb2 * 32 + 8 * g4 + 4 * hf;
-            float4 l4 = *reinterpret_cast<const float4*>(&slse_[ql]);
-            float4 d4 = *reinterpret_cast<const float4*>(&sdl_[ql]);
-            float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g4 + e;
-              float x = fast_exp2(st[r] * s.scale_log2 - la[e]);
-              if (!full && !visible(s, g, qbase + ql + e, kj)) x = 0.f;
-              pr[r] = x;
-              ds[r] = x * (dp[r] - da[e]);
-            }
-          }
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            pf[2 * qb2 + h2] = make_uint4(pack2<BF>(pr[8 * h2], pr[8 * h2 + 1]), pack2<BF>(pr[8 * h2 + 2], pr[8 * h2 + 3]),
-                                          pack2<BF>(pr[8 * h2 + 4], pr[8 * h2 + 5]), pack2<BF>(pr[8 * h2 + 6], pr[8 * h2 + 7]));
-            dsf[2 * qb2 + h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
-                                           pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
-          }
+        for (int c = 0; c < 2; ++c) {
+          const int off = (db * 32 + l32) * T::TP + 32 * qhalf + 16 * c + 8 * hf;
+          uint4 a = *reinterpret_cast<const uint4*>(&sgt_[off]);
+          uint4 b2 = *reinterpret_cast<const uint4*>(&sqt_[off]);
+          adv[db] = mfma16<BF>(a, pf[c], adv[db]);
+          adk[db] = mfma16<BF>(b2, dsf[c], adk[db]);
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int c = 0; c < NQC; ++c) {
-            uint4 a = *reinterpret_cast<const uint4*>(&sgt_[(db * 32 + l32) * T::TP + 16 * c + 8 * hf]);
-            adv[db] = mfma16<BF>(a, pf[c], adv[db]);
-            uint4 b2 = *reinterpret_cast<const uint4*>(&sqt_[(db * 32 + l32) * T::TP + 16 * c + 8 * hf]);
-            adk[db] = mfma16<BF>(b2, dsf[c], adk[db]);
-          }
-        }
-      }
     }
   }
-  if (kvalid) {
+  // sum the two query halves: qhalf 1 parks its partials in LDS, qhalf 0 adds and writes
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  if (qhalf == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[(((kblk * 2 + 0) * NDB + db) * 16 + r) * 64 + lane] = adk[db][r];
+        red[(((kblk * 2 + 1) * NDB + db) * 16 + r) * 64 + lane] = adv[db][r];
+      }
+  }
+  __syncthreads();
+  if (qhalf == 0 && kvalid) {
     uint16_t* krow = dkb + kj * p.dk.ss;
     uint16_t* vrow = dvb + kj * p.dv.ss;
 #pragma unroll
@@ -417,8 +467,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv16_kernel(BwdParams p) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d = db * 32 + 8 * gq + 4 * hf;
-        float a[4] = {adk[db][4 * gq], adk[db][4 * gq + 1], adk[db][4 * gq + 2], adk[db][4 * gq + 3]};
-        float b2[4] = {adv[db][4 * gq], adv[db][4 * gq + 1], adv[db][4 * gq + 2], adv[db][4 * gq + 3]};
+        float a[4], b2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * gq + e;
+          a[e] = adk[db][r] + red[(((kblk * 2 + 0) * NDB + db) * 16 + r) * 64 + lane];
+          b2[e] = adv[db][r] + red[(((kblk * 2 + 1) * NDB + db) * 16 + r) * 64 + lane];
+        }
         out4_16<BF>(krow + d, a, s.scale, p.aligned & kAlDK, p.accumulate);
         out4_16<BF>(vrow + d, b2, 1.f, p.aligned & kAlDV, p.accumulate);
       }
@@ -438,9 +493,9 @@ struct Tile32 {
   __device__ __forceinline__ void load(const float* base, int64_t ss, int row0, int nrows, bool al) {
 #pragma unroll
     for (int u = 0; u < LDC; ++u) {
-      int ci = threadIdx.x + u * kThreads;
-      int row = row0 + ci / (D / 4), col = (ci % (D / 4)) * 4;
-      r[u] = row < nrows ? load16<4>(base + row * ss + col, al) : make_uint4(0, 0, 0, 0);
+      const int ci = threadIdx.x + u * kThreads;
+      const int row = min(row0 + ci / (D / 4), nrows - 1), col = (ci % (D / 4)) * 4;
+      r[u] = load16<4>(base + int64_t(row) * ss + col, al);
     }
   }
   __device__ __forceinline__ void store(float* lds) const {
@@ -454,7 +509,7 @@ struct Tile32 {
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
-  constexpr int BM = kBwdQ, BN = 32, H2 = D / 2, NDB = D / 32;
+  constexpr int BM = kBwdQ32, BN = 32, H2 = D / 2, NDB = D / 32;
   using T = Tile32<D>;
   __shared__ __align__(16) float sk_[BN * T::RP];
   __shared__ __align__(16) float sv_[BN * T::RP];
@@ -554,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
-  constexpr int BK = kBwdK, BQ = 32, H2 = D / 2, NDB = D / 32;
+  constexpr int BK = kBwdK32, BQ = 32, H2 = D / 2, NDB = D / 32;
   using T = Tile32<D>;
   __shared__ __align__(16) float sq_[BQ * T::RP];
   __shared__ __align__(16) float sg_[BQ * T::RP];
@@ -719,10 +774,9 @@ hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
   hipError_t e = dt == DType::F32 ? pre<4, false>(p, st)
                                    : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
   if (e != hipSuccess) return e;
-  int64_t bq = s.thd ? ((s.total_q + kBwdQ - 1) / kBwdQ + s.batch) * s.hq
-                     : int64_t((s.sq + kBwdQ - 1) / kBwdQ) * s.batch * s.hq;
-  int64_t bk = s.thd ? ((s.total_k + kBwdK - 1) / kBwdK + s.batch) * s.hk
-                     : int64_t((s.sk + kBwdK - 1) / kBwdK) * s.batch * s.hk;
+  const int tq = dt == DType::F32 ? kBwdQ32 : kBwdQ16, tk = dt == DType::F32 ? kBwdK32 : kBwdK16;
+  int64_t bq = s.thd ? ((s.total_q + tq - 1) / tq + s.batch) * s.hq : int64_t((s.sq + tq - 1) / tq) * s.batch * s.hq;
+  int64_t bk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk : int64_t((s.sk + tk - 1) / tk) * s.batch * s.hk;
   switch (dt) {
     case DType::BF16:
       if (s.d == 32) return main16<true, 32>(p, st, bq, bk);

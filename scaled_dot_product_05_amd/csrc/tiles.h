@@ -28,12 +28,15 @@ constexpr int kFwdBN16_D128 = SDPA_FWD_BN_D128;
 constexpr int kFwdMinB_D128 = SDPA_FWD_MINB_D128;
 constexpr int kFwdBN32 = 32;  // keys per K/V tile, fp32 inputs
 
-// backward dQ: one workgroup owns kBwdQ query rows (32 per wave); keys stream in kBwdQInner tiles
-constexpr int kBwdQ = 128;
+// backward dQ: one workgroup owns kBwdQ16 (16-bit) or kBwdQ32 (fp32) query rows; keys stream
+// in kBwdQInner tiles (16-bit) or 32-key tiles (fp32)
+constexpr int kBwdQ16 = 64;
+constexpr int kBwdQ32 = 128;
 constexpr int kBwdQInner = 64;
-// backward dK/dV: one workgroup owns kBwdK keys (32 per wave) of one (batch, kv head);
-// query rows of every head of the group stream in kBwdKInner tiles
-constexpr int kBwdK = 128;
+// backward dK/dV: one workgroup owns kBwdK16 / kBwdK32 keys of one (batch, kv head); query
+// rows of every head of the group stream in kBwdKInner tiles (16-bit) or 32-row tiles (fp32)
+constexpr int kBwdK16 = 64;
+constexpr int kBwdK32 = 128;
 constexpr int kBwdKInner = 64;
 
 // THD scheduler buckets (costs above the last bucket share it)
