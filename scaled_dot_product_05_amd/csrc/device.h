@@ -97,7 +97,83 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), acc, false);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// v_permlane32_swap_b32 with both operands x: the first result holds x of lanes 0-31 in
+// both halves, the second x of lanes 32-63 in both halves.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// x of the lane 32 away (lane l ^ 32), without an LDS round trip.
+__device__ __forceinline__ float xor32(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return (threadIdx.x & 32) ? lo : hi;
+}
+
+// max / sum of x over lanes l and l ^ 32; both lanes get the identical result.
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
+
+// LDS as a byte array in its own address space (ds_* instructions with immediate offsets).
+typedef __attribute__((address_space(3))) char lds_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(N): wait until at most N vector memory loads of this wave are in flight
+// (LDS and export counters left alone).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight (including loads
+// into LDS, which the caller waits for with vm_wait) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Buffer resource words over [base, base + bytes): loads past the end return zero per
+// dword.  Word 3 is the gfx9 default format with offset-only (raw) addressing.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = int32_t(bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes));
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xffff), n, 0x00020000};
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave lands at
+// dst + 16 * i (dst wave-uniform), read from the resource at byte offset voff.  Issued as
+// inline assembly so that the compiler does not order later LDS reads behind it (it
+// cannot tell which LDS bytes the load writes); the caller waits with vm_wait and a
+// barrier before the destination is read.
+__device__ __forceinline__ void dma16(i32x4_t r, lds_t* dst, uint32_t voff) {
+  const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds" : : "{m0}"(d), "v"(voff), "s"(r) : "memory");
+}
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_read16(const lds_t* p) {
+  return __builtin_bit_cast(uint4, *(const __attribute__((address_space(3))) u32x4_t*)p);
+}
+
+// ds_read_b64_tr_b16: lane 16g + 4a + b receives element b of the 8-byte rows addressed by
+// lanes 16g + a + 4c, c = 0..3, as its elements c.
+__device__ __forceinline__ uint2 read_tr16(const lds_t* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
 
 // 16 bytes from a row that is 16-byte aligned (al) or only element aligned.
 template <int ES>

@@ -30,13 +30,17 @@ struct WorkPos {
 };
 
 // Decode blockIdx.x into (sequence, q head, q tile).  Returns false for idle blocks.
-__device__ __forceinline__ bool decode_work(const Shape& s, const WorkItem* work,
-                                            const int32_t* count, int rows_per_tile, WorkPos& w) {
+// Padded layouts: the q tile index is outermost and reversed (longest tiles first under a
+// causal mask), (batch, head) fastest.  Workgroups are dispatched to the 8 XCDs round-robin,
+// so when batch * heads is a multiple of 8 every tile of one head runs on the same XCD and
+// shares its K/V rows through that XCD's L2.
+__device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_tile, WorkPos& w) {
+  const Shape& s = p.s;
   if (s.thd) {
     int item = blockIdx.x / s.hq;
     w.h = blockIdx.x % s.hq;
-    if (item >= *count) return false;
-    WorkItem it = work[item];
+    if (item >= *p.work_count) return false;
+    WorkItem it = p.work[item];
     w.b = it.seq;
     w.tile = it.tile;
     return true;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16_kernel(FwdParams p) {
 
   const Shape& s = p.s;
   WorkPos w;
-  if (!decode_work(s, p.work, p.work_count, BM, w)) return;
+  if (!decode_work(p, BM, w)) return;
   const Seq g = seq_of(s, w.b);
   const int q0 = w.tile * BM;
   if (q0 >= g.sq) return;
@@ -314,6 +318,286 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16_kernel(FwdParams p) {
 }
 
 // ----------------------------------------------------------------------------------------
+// bf16 / fp16 inputs, software-pipelined: the main path for 16-byte aligned rows.
+//
+// K and V tiles go from HBM straight into LDS (buffer loads with the LDS destination), so
+// no registers stage them and rows past the end of the sequence arrive as zeros.  Both
+// tiles stay row-major in LDS with their 16-byte chunks XOR-swizzled by row:
+//   K: chunk c of row r sits at slot c ^ swk(r), so the 32 rows one A-operand read touches
+//      spread over all banks;
+//   V: chunk c of row r sits at slot c ^ swv(r); V^T operands come from transposed LDS
+//      reads (ds_read_b64_tr_b16), two per 8-key contraction slot group.
+// The loop runs one tile ahead on the matrix cores: while the VALU turns tile t's scores
+// into probabilities, the QK^T products of tile t+1 are already issued, and the P V
+// products of tile t follow.  Loads for K(t+2) and V(t+1) are issued at the top of step t
+// and waited for at its end, one barrier per tile.
+// ----------------------------------------------------------------------------------------
+// LDS serves 256 bytes (64 banks) per cycle; a 16-byte read covers 16 lanes per cycle and
+// an 8-byte read 32 lanes.  K reads take one chunk of 16 consecutive rows, so those rows
+// must fall on 16 distinct 16-byte bank slots; transposed V reads take 4 consecutive rows
+// x 64 bytes per 32 lanes, so those 4 rows must fall on distinct 64-byte bank quarters.
+template <int CPR>
+__device__ __forceinline__ int swk(int r) {
+  return CPR >= 16 ? (r & 15) : CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+template <int CPR>
+__device__ __forceinline__ int swv(int r) {
+  return CPR >= 16 ? 4 * (r & 3) : CPR == 8 ? 2 * (r & 3) : 0;
+}
+
+template <bool BF, int D, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
+  constexpr int BM = 32 * kWaves;
+  constexpr int BN = kFwdBNP;
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int TB = BN * D * 2;          // bytes per K or V tile
+  constexpr int NDMA = BN * CPR / kThreads;  // DMA instructions per thread per tile
+  constexpr int NC = D / 16;              // contraction chunks of Q K^T
+  constexpr int NKB = BN / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NPC = BN / 16;            // contraction chunks of P V
+  static_assert(NDMA >= 1 && BN % 32 == 0, "tile split");
+  constexpr float kTau = 8.f;
+  constexpr int NS = D >= 128 ? kFwdStagesD128 : kFwdStages;  // K and V slots each
+  __shared__ __align__(16) char smem_[2 * NS * TB];  // K slots, then V slots
+  lds_t* const lds = (lds_t*)smem_;
+
+  const Shape& s = p.s;
+  WorkPos w;
+  if (!decode_work(p, BM, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hk = w.h / s.group;
+
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh +
+                       g.qrow0 * p.q.ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh +
+                       g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh +
+                       g.krow0 * p.v.ss;
+  uint16_t* ob = static_cast<uint16_t*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN;
+  const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  int kf0, kf1;
+  {
+    const int64_t lo_full = int64_t(qend - 1) + g.off + s.lo_rel;
+    const int64_t hi_full = min(int64_t(q0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
+    const int64_t a = lo_full <= 0 ? 0 : (lo_full + BN - 1) / BN;
+    const int64_t b = hi_full < 0 ? 0 : (hi_full + 1) / BN;
+    kf0 = int(clamp64(a, kt0, kt1));
+    kf1 = int(clamp64(b, kf0, kt1));
+  }
+  const int qw0 = q0 + wave * 32;
+  const int qw1 = min(qw0 + 32, g.sq);
+  const int qi = qw0 + l32;
+
+  const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
+  const uint32_t qsign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
+  uint4 qf[NC];
+  {
+    const int qr = min(qi, g.sq - 1);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      uint4 t = *reinterpret_cast<const uint4*>(qb + qr * p.q.ss + 16 * cc + 8 * hf);
+      qf[cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
+    }
+  }
+
+  // ---- HBM -> LDS ----
+  const int64_t kss = p.k.ss, vss = p.v.ss;
+  uint32_t koff_g[NDMA], voff_g[NDMA];
+#pragma unroll
+  for (int u = 0; u < NDMA; ++u) {
+    const int P = (u * kWaves + wave) * 64 + lane;
+    const int row = P / CPR, pos = P % CPR;
+    koff_g[u] = uint32_t(row * kss * 2 + ((pos ^ swk<CPR>(row)) * 16));
+    voff_g[u] = uint32_t(row * vss * 2 + ((pos ^ swv<CPR>(row)) * 16));
+  }
+  auto issue_k = [&](int t, int buf) {
+    const auto r = make_rsrc(kb + int64_t(t) * BN * kss, (int64_t(g.sk) - int64_t(t) * BN - 1) * kss * 2 + D * 2);
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(r, lds + buf * TB + (u * kWaves + wave) * 1024, koff_g[u]);
+  };
+  auto issue_v = [&](int t, int buf) {
+    const auto r = make_rsrc(vb + int64_t(t) * BN * vss, (int64_t(g.sk) - int64_t(t) * BN - 1) * vss * 2 + D * 2);
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(r, lds + (NS + buf) * TB + (u * kWaves + wave) * 1024, voff_g[u]);
+  };
+
+  // ---- LDS operand addresses (lane part; tile, block and buffer parts are immediates) ----
+  int ka[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) ka[cc] = (l32 * CPR + ((2 * cc + hf) ^ swk<CPR>(l32))) * 16;
+  int va[NDB];
+  {
+    const int gg = lane >> 4, cr = (lane >> 2) & 3, a = lane & 3;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      va[db] = ((4 * (gg >> 1) + cr) * CPR + ((4 * db + 2 * (gg & 1) + (a >> 1)) ^ swv<CPR>(cr))) * 16 +
+               (a & 1) * 8;
+  }
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+  float m_run = kNegInf, l_run = 0.f;
+
+  // The key blocks are independent accumulation chains; alternating them keeps the
+  // previous product of a chain in flight while the next one issues.
+  auto scores = [&](auto B, f32x16_t(&st)[NKB]) {
+    constexpr int b = decltype(B)::value;
+#pragma unroll
+    for (int k2 = 0; k2 < NKB; ++k2) st[k2] = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2) {
+        const uint4 a = lds_read16(lds + b * TB + k2 * 32 * CPR * 16 + ka[cc]);
+        st[k2] = mfma16<BF>(a, qf[cc], st[k2]);
+      }
+  };
+  auto pv = [&](auto B, const uint4(&pf)[NPC]) {
+    constexpr int b = decltype(B)::value;
+#pragma unroll
+    for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_t* base = lds + (NS + b) * TB + 16 * cc * CPR * 16 + va[db];
+        const uint2 lo = read_tr16(base), hi = read_tr16(base + 8 * CPR * 16);
+        acc[db] = mfma16<BF>(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[cc], acc[db]);
+      }
+  };
+  auto mask = [&](int t, f32x16_t(&st)[NKB]) {
+    const int kbase = t * BN;
+    if (!(t >= kf0 && t < kf1) && !tile_full(s, g, qw0, qw1, kbase, kbase + BN)) {
+      const int base_rel = kbase - qi - g.off + 4 * hf;
+      const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
+          st[k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[k2][r] : kNegInf;
+        }
+    }
+  };
+  auto softmax_ref = [&](const f32x16_t(&st)[NKB]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[k2][r]);
+    mx = max_halves(mx);
+    const float m_tile = mx == kNegInf ? kNegInf : mx * c;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau) != 0) {
+      const bool raise = m_tile > m_run + kTau;
+      const float alpha = raise ? fast_exp2(m_run - m_tile) : 1.f;
+      m_run = raise ? m_tile : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+  };
+  auto probs = [&](const f32x16_t(&st)[NKB], uint4(&pf)[NPC]) {
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NPC; ++cc) {
+      const int k2 = cc >> 1, rb = (cc & 1) * 8;
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = fast_exp2(__builtin_fmaf(st[k2][rb + j], c, -m_use));
+      ps0 += (e[0] + e[1]) + (e[2] + e[3]);
+      ps1 += (e[4] + e[5]) + (e[6] + e[7]);
+      pf[cc] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
+                          pack2<BF>(e[6], e[7]));
+    }
+    l_run += ps0 + ps1;
+  };
+
+  // Slots: K(t) lives in K slot t % NS, V(t) in V slot t % NS.  Step t reads K(t+1) (the
+  // next tile's scores) and V(t), issues the loads of K(t+NS) and V(t+NS-1), and before its
+  // barrier waits only for the loads issued one step earlier (NS = 3) or for all (NS = 2).
+  // Loads are issued whether or not the tile exists: past the sequence end the buffer
+  // range is empty and the slot fills with zeros, which keeps the wait counts fixed.
+  const int n = kt1 - kt0;
+  f32x16_t sa[NKB], sb[NKB];
+  if (n > 0) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      issue_k(kt0 + j, j);
+      if (j + 1 < NS) issue_v(kt0 + j, j);
+    }
+    vm_wait<2 * (NS - 2) * NDMA>();
+    lds_barrier();
+    scores(std::integral_constant<int, 0>(), sa);
+  }
+  // step i (phase I = i % U): the scores of tile kt0+i are in `cur`.  The QK^T products of
+  // the next tile are issued even past the last tile (their result is then unused), so a
+  // step has no branch between the two cases.
+  auto step = [&](auto I, int i, f32x16_t(&cur)[NKB], f32x16_t(&nxt)[NKB]) {
+    constexpr int ph = decltype(I)::value % NS;
+    const int t = kt0 + i;
+    issue_k(t + NS, ph);
+    issue_v(t + NS - 1, (ph + NS - 1) % NS);
+    mask(t, cur);
+    softmax_ref(cur);
+    uint4 pf[NPC];
+    scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
+    probs(cur, pf);
+    pv(std::integral_constant<int, ph>(), pf);
+    vm_wait<2 * (NS - 2) * NDMA>();
+    lds_barrier();
+  };
+  constexpr int U = NS == 2 ? 2 : 6;  // a multiple of NS and of the two score buffers
+  for (int i = 0; i < n; i += U) {
+    step(std::integral_constant<int, 0>(), i, sa, sb);
+    if (i + 1 >= n) break;
+    step(std::integral_constant<int, 1>(), i + 1, sb, sa);
+    if constexpr (U > 2) {
+      if (i + 2 >= n) break;
+      step(std::integral_constant<int, 2>(), i + 2, sa, sb);
+      if (i + 3 >= n) break;
+      step(std::integral_constant<int, 3>(), i + 3, sb, sa);
+      if (i + 4 >= n) break;
+      step(std::integral_constant<int, 4>(), i + 4, sa, sb);
+      if (i + 5 >= n) break;
+      step(std::integral_constant<int, 5>(), i + 5, sb, sa);
+    }
+  }
+  vm_wait<0>();  // no load may land in LDS after the workgroup ends
+
+  const float lt = sum_halves(l_run);
+  if (qi < g.sq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = ob + qi * p.o.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        int d = db * 32 + 8 * gq + 4 * hf;
+        uint32_t lo = pack2<BF>(acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv);
+        uint32_t hi = pack2<BF>(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo, hi);
+      }
+    }
+    if (hf == 0 && p.lse.ptr) {
+      float* lp = p.lse.ptr + w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
+      *lp = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // fp32 inputs.  Nothing is rounded below fp32 (PyTorch issue 135161 traces its large
 // gradient errors to a tensor-core shortcut inside an "fp32" kernel), and the scores are
 // formed in fp64: fp32 inputs widen exactly, v_mfma_f64_16x16x4 accumulates q.k in fp64,
@@ -339,7 +623,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdPa
 
   const Shape& s = p.s;
   WorkPos w;
-  if (!decode_work(s, p.work, p.work_count, BM, w)) return;
+  if (!decode_work(p, BM, w)) return;
   const Seq g = seq_of(s, w.b);
   const int q0 = w.tile * BM;
   if (q0 >= g.sq) return;
@@ -509,6 +793,15 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdPa
   }
 }
 
+// Grid for a tile of `rows` query rows: THD uses the scheduler's work list (rows past the
+// packed total plus one partial tile per sequence), padded layouts one block per tile.
+static int64_t fwd_grid(const FwdParams& p, int rows) {
+  const Shape& s = p.s;
+  const int64_t tiles = s.thd ? (s.total_q + rows - 1) / rows + s.batch
+                              : int64_t((s.sq + rows - 1) / rows) * s.batch;
+  return tiles * s.hq;
+}
+
 template <class K>
 static hipError_t go(K kernel, int blocks, hipStream_t st, const FwdParams& p) {
   prof_begin(st, "attn_fwd");
@@ -519,13 +812,18 @@ static hipError_t go(K kernel, int blocks, hipStream_t st, const FwdParams& p) {
 
 template <bool BF, int D, int BN, int MINB>
 static hipError_t go16(const FwdParams& p, hipStream_t st) {
-  const Shape& s = p.s;
   constexpr int BM = 32 * kWaves;
   static_assert(BM == kFwdBM16, "host and kernel tile rows differ");
-  int64_t blocks = s.thd ? (s.total_q + BM - 1) / BM + s.batch : int64_t((s.sq + BM - 1) / BM) * s.batch;
-  blocks *= s.hq;
+  const int64_t blocks = fwd_grid(p, BM);
   if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const bool al = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
+  // The pipelined kernel addresses K/V rows with 32-bit buffer offsets (a tile spans
+  // kFwdBNP rows) and relies on rows of at least D elements, so that every row past the
+  // sequence end lies wholly outside the buffer range.
+  const int64_t kv_ss = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
+  const bool pipe = al && p.k.ss >= D && p.v.ss >= D && int64_t(kFwdBNP) * kv_ss * 2 < (int64_t(1) << 31);
+  if (pipe) return go(fwd16p_kernel<BF, D, MINB>, int(blocks), st, p);
   return al ? go(fwd16_kernel<BF, D, BN, MINB, true>, int(blocks), st, p)
             : go(fwd16_kernel<BF, D, BN, MINB, false>, int(blocks), st, p);
 }
@@ -543,10 +841,9 @@ hipError_t launch_fwd(const FwdParams& p, DType dt, hipStream_t st) {
   const Shape& s = p.s;
   if (dt == DType::BF16) return fwd16_dispatch<true>(p, st);
   if (dt == DType::F16) return fwd16_dispatch<false>(p, st);
-  int64_t blocks = s.thd ? (s.total_q + kFwdBM - 1) / kFwdBM + s.batch
-                         : int64_t((s.sq + kFwdBM - 1) / kFwdBM) * s.batch;
-  blocks *= s.hq;
+  const int64_t blocks = fwd_grid(p, kFwdBM);
   if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (s.d == 32) return go(fwd32_kernel<32>, int(blocks), st, p);
   if (s.d == 64) return go(fwd32_kernel<64>, int(blocks), st, p);
   return go(fwd32_kernel<128>, int(blocks), st, p);

@@ -27,6 +27,18 @@ constexpr int kFwdMinB_D64 = SDPA_FWD_MINB_D64;  // per CU, head_dim 64
 constexpr int kFwdBN16_D128 = SDPA_FWD_BN_D128;
 constexpr int kFwdMinB_D128 = SDPA_FWD_MINB_D128;
 constexpr int kFwdBN32 = 32;  // keys per K/V tile, fp32 inputs
+#ifndef SDPA_FWD_BNP
+#define SDPA_FWD_BNP 64
+#endif
+constexpr int kFwdBNP = SDPA_FWD_BNP;  // keys per K/V tile, pipelined 16-bit kernel
+#ifndef SDPA_FWD_NS
+#define SDPA_FWD_NS 3
+#endif
+#ifndef SDPA_FWD_NS_D128
+#define SDPA_FWD_NS_D128 2
+#endif
+constexpr int kFwdStages = SDPA_FWD_NS;            // K/V LDS slots, head_dim <= 64
+constexpr int kFwdStagesD128 = SDPA_FWD_NS_D128;  // K/V LDS slots, head_dim 128
 
 // backward dQ: one workgroup owns kBwdQ16 (16-bit) or kBwdQ32 (fp32) query rows; keys stream
 // in kBwdQInner tiles (16-bit) or 32-key tiles (fp32)
