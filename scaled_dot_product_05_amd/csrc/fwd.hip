@@ -345,10 +345,11 @@ __device__ __forceinline__ int swv(int r) {
   return CPR >= 16 ? 4 * (r & 3) : CPR == 8 ? 2 * (r & 3) : 0;
 }
 
-template <bool BF, int D, int MINB>
+// QB = query blocks of 32 per wave: with QB = 2 every K or V operand read from LDS feeds two
+// products, halving LDS reads per flop, and each K/V tile serves 256 query rows.
+template <bool BF, int D, int MINB, int QB, int BN>
 __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
-  constexpr int BM = 32 * kWaves;
-  constexpr int BN = kFwdBNP;
+  constexpr int BM = 32 * QB * kWaves;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TB = BN * D * 2;          // bytes per K or V tile
   constexpr int NDMA = BN * CPR / kThreads;  // DMA instructions per thread per tile
@@ -385,28 +386,30 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   key_range(s, g, q0, qend, j0, j1);
   const int kt0 = j0 / BN;
   const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
-  int kf0, kf1;
-  {
-    const int64_t lo_full = int64_t(qend - 1) + g.off + s.lo_rel;
-    const int64_t hi_full = min(int64_t(q0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
+  const int qw0 = q0 + wave * 32 * QB;
+  const int qw1 = min(qw0 + 32 * QB, g.sq);
+  // key tiles [wf0, wf1) that every row of this wave sees in full (no mask needed); a wave
+  // without rows masks everything (its lanes are never stored)
+  int wf0 = 0, wf1 = 0;
+  if (qw0 < qw1) {
+    const int64_t lo_full = int64_t(qw1 - 1) + g.off + s.lo_rel;
+    const int64_t hi_full = min(int64_t(qw0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
     const int64_t a = lo_full <= 0 ? 0 : (lo_full + BN - 1) / BN;
     const int64_t b = hi_full < 0 ? 0 : (hi_full + 1) / BN;
-    kf0 = int(clamp64(a, kt0, kt1));
-    kf1 = int(clamp64(b, kf0, kt1));
+    wf0 = int(clamp64(a, 0, int64_t(1) << 30));
+    wf1 = int(clamp64(b, wf0, int64_t(1) << 30));
   }
-  const int qw0 = q0 + wave * 32;
-  const int qw1 = min(qw0 + 32, g.sq);
-  const int qi = qw0 + l32;
 
   const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
   const uint32_t qsign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
-  uint4 qf[NC];
-  {
-    const int qr = min(qi, g.sq - 1);
+  uint4 qf[QB][NC];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int qr = min(qw0 + 32 * j + l32, g.sq - 1);
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       uint4 t = *reinterpret_cast<const uint4*>(qb + qr * p.q.ss + 16 * cc + 8 * hf);
-      qf[cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
+      qf[j][cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
     }
   }
 
@@ -420,15 +423,20 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
     koff_g[u] = uint32_t(row * kss * 2 + ((pos ^ swk<CPR>(row)) * 16));
     voff_g[u] = uint32_t(row * vss * 2 + ((pos ^ swv<CPR>(row)) * 16));
   }
+  // One resource per tensor over the sequence's rows; a tile is a 32-bit offset (the host
+  // guarantees that every tile issued, up to NS past the last, stays below 2^31 bytes).
+  const i32x4_t rk = make_rsrc(kb, (int64_t(g.sk) - 1) * kss * 2 + D * 2);
+  const i32x4_t rv = make_rsrc(vb, (int64_t(g.sk) - 1) * vss * 2 + D * 2);
+  const uint32_t kstep = uint32_t(BN * kss * 2), vstep = uint32_t(BN * vss * 2);
   auto issue_k = [&](int t, int buf) {
-    const auto r = make_rsrc(kb + int64_t(t) * BN * kss, (int64_t(g.sk) - int64_t(t) * BN - 1) * kss * 2 + D * 2);
+    const uint32_t o = uint32_t(t) * kstep;
 #pragma unroll
-    for (int u = 0; u < NDMA; ++u) dma16(r, lds + buf * TB + (u * kWaves + wave) * 1024, koff_g[u]);
+    for (int u = 0; u < NDMA; ++u) dma16(rk, lds + buf * TB + (u * kWaves + wave) * 1024, koff_g[u] + o);
   };
   auto issue_v = [&](int t, int buf) {
-    const auto r = make_rsrc(vb + int64_t(t) * BN * vss, (int64_t(g.sk) - int64_t(t) * BN - 1) * vss * 2 + D * 2);
+    const uint32_t o = uint32_t(t) * vstep;
 #pragma unroll
-    for (int u = 0; u < NDMA; ++u) dma16(r, lds + (NS + buf) * TB + (u * kWaves + wave) * 1024, voff_g[u]);
+    for (int u = 0; u < NDMA; ++u) dma16(rv, lds + (NS + buf) * TB + (u * kWaves + wave) * 1024, voff_g[u] + o);
   };
 
   // ---- LDS operand addresses (lane part; tile, block and buffer parts are immediates) ----
@@ -444,26 +452,34 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
                (a & 1) * 8;
   }
 
-  f32x16_t acc[NDB];
+  f32x16_t acc[QB][NDB];
+  float m_run[QB], l_run[QB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
-  float m_run = kNegInf, l_run = 0.f;
+  for (int j = 0; j < QB; ++j) {
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[j][i] = zero16();
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+  }
 
-  // The key blocks are independent accumulation chains; alternating them keeps the
-  // previous product of a chain in flight while the next one issues.
-  auto scores = [&](auto B, f32x16_t(&st)[NKB]) {
+  // The key blocks and query blocks are independent accumulation chains; alternating them
+  // keeps the previous product of a chain in flight while the next one issues.
+  auto scores = [&](auto B, f32x16_t(&st)[QB][NKB]) {
     constexpr int b = decltype(B)::value;
 #pragma unroll
-    for (int k2 = 0; k2 < NKB; ++k2) st[k2] = zero16();
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2) st[j][k2] = zero16();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int k2 = 0; k2 < NKB; ++k2) {
         const uint4 a = lds_read16(lds + b * TB + k2 * 32 * CPR * 16 + ka[cc]);
-        st[k2] = mfma16<BF>(a, qf[cc], st[k2]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) st[j][k2] = mfma16<BF>(a, qf[j][cc], st[j][k2]);
       }
   };
-  auto pv = [&](auto B, const uint4(&pf)[NPC]) {
+  auto pv = [&](auto B, const uint4(&pf)[QB][NPC]) {
     constexpr int b = decltype(B)::value;
 #pragma unroll
     for (int cc = 0; cc < NPC; ++cc)
@@ -471,57 +487,80 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
       for (int db = 0; db < NDB; ++db) {
         const lds_t* base = lds + (NS + b) * TB + 16 * cc * CPR * 16 + va[db];
         const uint2 lo = read_tr16(base), hi = read_tr16(base + 8 * CPR * 16);
-        acc[db] = mfma16<BF>(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[cc], acc[db]);
+        const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) acc[j][db] = mfma16<BF>(a, pf[j][cc], acc[j][db]);
       }
   };
-  auto mask = [&](int t, f32x16_t(&st)[NKB]) {
+  // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
+  auto mask = [&](int t, f32x16_t(&st)[QB][NKB]) {
     const int kbase = t * BN;
-    if (!(t >= kf0 && t < kf1) && !tile_full(s, g, qw0, qw1, kbase, kbase + BN)) {
-      const int base_rel = kbase - qi - g.off + 4 * hf;
-      const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+    if (t < wf0 || t >= wf1) {
+      // keeps the compiler from evaluating the mask on every tile as selects
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const int qi = qw0 + 32 * j + l32;
+        const int base_rel = kbase - qi - g.off + 4 * hf;
+        const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+#pragma unroll
+        for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
+            st[j][k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[j][k2][r] : kNegInf;
+          }
+      }
+    }
+  };
+  // Lazy rescaling: the reference max only moves when a tile's max exceeds it by more than
+  // kTau (log2 units), so P <= 2^kTau and the O accumulator is rarely rescaled.
+  auto softmax_ref = [&](const f32x16_t(&st)[QB][NKB]) {
+    float m_tile[QB];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float mx = kNegInf;
 #pragma unroll
       for (int k2 = 0; k2 < NKB; ++k2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
-          st[k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[k2][r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[j][k2][r]);
+      mx = max_halves(mx);
+      m_tile[j] = mx == kNegInf ? kNegInf : mx * c;
+      any = any || (m_tile[j] > m_run[j] + kTau);
+    }
+    if (__builtin_amdgcn_ballot_w64(any) != 0) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const bool raise = m_tile[j] > m_run[j] + kTau;
+        const float alpha = raise ? fast_exp2(m_run[j] - m_tile[j]) : 1.f;
+        m_run[j] = raise ? m_tile[j] : m_run[j];
+        l_run[j] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][db][r] *= alpha;
+      }
     }
   };
-  auto softmax_ref = [&](const f32x16_t(&st)[NKB]) {
-    float mx = kNegInf;
+  auto probs = [&](const f32x16_t(&st)[QB][NKB], uint4(&pf)[QB][NPC]) {
 #pragma unroll
-    for (int k2 = 0; k2 < NKB; ++k2)
+    for (int j = 0; j < QB; ++j) {
+      const float m_use = m_run[j] == kNegInf ? 0.f : m_run[j];
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[k2][r]);
-    mx = max_halves(mx);
-    const float m_tile = mx == kNegInf ? kNegInf : mx * c;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau) != 0) {
-      const bool raise = m_tile > m_run + kTau;
-      const float alpha = raise ? fast_exp2(m_run - m_tile) : 1.f;
-      m_run = raise ? m_tile : m_run;
-      l_run *= alpha;
+      for (int cc = 0; cc < NPC; ++cc) {
+        const int k2 = cc >> 1, rb = (cc & 1) * 8;
+        float e[8];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(__builtin_fmaf(st[j][k2][rb + i], c, -m_use));
+        ps0 += (e[0] + e[1]) + (e[2] + e[3]);
+        ps1 += (e[4] + e[5]) + (e[6] + e[7]);
+        pf[j][cc] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
+                               pack2<BF>(e[6], e[7]));
+      }
+      l_run[j] += ps0 + ps1;
     }
-  };
-  auto probs = [&](const f32x16_t(&st)[NKB], uint4(&pf)[NPC]) {
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < NPC; ++cc) {
-      const int k2 = cc >> 1, rb = (cc & 1) * 8;
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = fast_exp2(__builtin_fmaf(st[k2][rb + j], c, -m_use));
-      ps0 += (e[0] + e[1]) + (e[2] + e[3]);
-      ps1 += (e[4] + e[5]) + (e[6] + e[7]);
-      pf[cc] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
-                          pack2<BF>(e[6], e[7]));
-    }
-    l_run += ps0 + ps1;
   };
 
   // Slots: K(t) lives in K slot t % NS, V(t) in V slot t % NS.  Step t reads K(t+1) (the
@@ -530,7 +569,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   // Loads are issued whether or not the tile exists: past the sequence end the buffer
   // range is empty and the slot fills with zeros, which keeps the wait counts fixed.
   const int n = kt1 - kt0;
-  f32x16_t sa[NKB], sb[NKB];
+  f32x16_t sa[QB][NKB], sb[QB][NKB];
   if (n > 0) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -540,18 +579,20 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
     vm_wait<2 * (NS - 2) * NDMA>();
     lds_barrier();
     scores(std::integral_constant<int, 0>(), sa);
+    // step 0 reloads K slot 0: every wave must be done reading it first
+    lds_barrier();
   }
   // step i (phase I = i % U): the scores of tile kt0+i are in `cur`.  The QK^T products of
   // the next tile are issued even past the last tile (their result is then unused), so a
   // step has no branch between the two cases.
-  auto step = [&](auto I, int i, f32x16_t(&cur)[NKB], f32x16_t(&nxt)[NKB]) {
+  auto step = [&](auto I, int i, f32x16_t(&cur)[QB][NKB], f32x16_t(&nxt)[QB][NKB]) {
     constexpr int ph = decltype(I)::value % NS;
     const int t = kt0 + i;
     issue_k(t + NS, ph);
     issue_v(t + NS - 1, (ph + NS - 1) % NS);
     mask(t, cur);
     softmax_ref(cur);
-    uint4 pf[NPC];
+    uint4 pf[QB][NPC];
     scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
     probs(cur, pf);
     pv(std::integral_constant<int, ph>(), pf);
@@ -576,23 +617,27 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
-  const float lt = sum_halves(l_run);
-  if (qi < g.sq) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow = ob + qi * p.o.ss;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int j = 0; j < QB; ++j) {
+    const float lt = sum_halves(l_run[j]);
+    const int qi = qw0 + 32 * j + l32;
+    if (qi < g.sq) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* orow = ob + qi * p.o.ss;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        int d = db * 32 + 8 * gq + 4 * hf;
-        uint32_t lo = pack2<BF>(acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv);
-        uint32_t hi = pack2<BF>(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo, hi);
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          int d = db * 32 + 8 * gq + 4 * hf;
+          uint32_t lo = pack2<BF>(acc[j][db][4 * gq] * inv, acc[j][db][4 * gq + 1] * inv);
+          uint32_t hi = pack2<BF>(acc[j][db][4 * gq + 2] * inv, acc[j][db][4 * gq + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo, hi);
+        }
       }
-    }
-    if (hf == 0 && p.lse.ptr) {
-      float* lp = p.lse.ptr + w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
-      *lp = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
+      if (hf == 0 && p.lse.ptr) {
+        float* lp = p.lse.ptr + w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
+        *lp = lt > 0.f ? (m_run[j] + __log2f(lt)) * kLn2 : kNegInf;
+      }
     }
   }
 }
@@ -817,13 +862,23 @@ static hipError_t go16(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = fwd_grid(p, BM);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t kv_ss0 = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
+  const bool al0 = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
+  if constexpr (D == 64 && kFwdWideD64) {
+    // 64 query rows per wave when the grid still fills the chip twice over
+    const int64_t wide = fwd_grid(p, 2 * BM);
+    if (al0 && p.k.ss >= D && p.v.ss >= D && (int64_t(p.s.sk) + 4 * 32) * kv_ss0 * 2 < (int64_t(1) << 31) &&
+        !p.s.thd && wide >= kFwdWideMinBlocks)
+      return go(fwd16p_kernel<BF, D, MINB, 2, 32>, int(wide), st, p);
+  }
   const bool al = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
   // The pipelined kernel addresses K/V rows with 32-bit buffer offsets (a tile spans
   // kFwdBNP rows) and relies on rows of at least D elements, so that every row past the
   // sequence end lies wholly outside the buffer range.
   const int64_t kv_ss = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
-  const bool pipe = al && p.k.ss >= D && p.v.ss >= D && int64_t(kFwdBNP) * kv_ss * 2 < (int64_t(1) << 31);
-  if (pipe) return go(fwd16p_kernel<BF, D, MINB>, int(blocks), st, p);
+  const bool pipe = al && p.k.ss >= D && p.v.ss >= D &&
+                    (int64_t(p.s.sk) + 4 * kFwdBNP) * kv_ss * 2 < (int64_t(1) << 31);
+  if (pipe) return go(fwd16p_kernel<BF, D, MINB, 1, kFwdBNP>, int(blocks), st, p);
   return al ? go(fwd16_kernel<BF, D, BN, MINB, true>, int(blocks), st, p)
             : go(fwd16_kernel<BF, D, BN, MINB, false>, int(blocks), st, p);
 }

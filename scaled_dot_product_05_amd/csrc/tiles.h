@@ -39,6 +39,14 @@ constexpr int kFwdBNP = SDPA_FWD_BNP;  // keys per K/V tile, pipelined 16-bit ke
 #endif
 constexpr int kFwdStages = SDPA_FWD_NS;            // K/V LDS slots, head_dim <= 64
 constexpr int kFwdStagesD128 = SDPA_FWD_NS_D128;  // K/V LDS slots, head_dim 128
+#ifndef SDPA_FWD_WIDE_D64
+#define SDPA_FWD_WIDE_D64 0
+#endif
+#ifndef SDPA_FWD_WIDE_MIN
+#define SDPA_FWD_WIDE_MIN 1024
+#endif
+constexpr bool kFwdWideD64 = SDPA_FWD_WIDE_D64;      // 64 query rows per wave, head_dim 64
+constexpr int kFwdWideMinBlocks = SDPA_FWD_WIDE_MIN;  // ... when the grid has this many blocks
 
 // backward dQ: one workgroup owns kBwdQ16 (16-bit) or kBwdQ32 (fp32) query rows; keys stream
 // in kBwdQInner tiles (16-bit) or 32-key tiles (fp32)
