@@ -158,8 +158,8 @@ int sdpa_fwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
              const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward workspace size in bytes: fp32 Delta_i = dO_i . O_i - dLSE_i for every q row,
- * plus the THD work lists.  Host only. */
+/* Backward workspace size in bytes: fp32 Delta_i = dO_i . O_i - dLSE_i and fp32
+ * LSE_i * log2(e) for every q row, plus the THD work lists.  Host only. */
 int sdpa_bwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes);
 
 /* Host-only dry run of sdpa_bwd's validation. */

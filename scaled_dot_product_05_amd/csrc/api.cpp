@@ -326,7 +326,7 @@ size_t fwd_ws_bytes(const Shape& s, int32_t dtype) {
 }
 
 struct BwdWs {
-  int64_t delta_off, wq_off, cq_off, wk_off, ck_off, total;
+  int64_t delta_off, lse2_off, wq_off, cq_off, wk_off, ck_off, total;
 };
 
 int bwd_q_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdQ32 : kBwdQ16; }
@@ -336,7 +336,8 @@ BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
   BwdWs w{};
   int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
   w.delta_off = 0;
-  int64_t off = round_up(rows * 4, 256);
+  w.lse2_off = round_up(rows * 4, 256);
+  int64_t off = round_up(w.lse2_off + rows * 4, 256);
   if (s.thd) {
     w.wq_off = off;
     off = round_up(off + thd_items(s.total_q, s.batch, bwd_q_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
@@ -667,6 +668,8 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   if (a.s.batch == 0 || (a.rows_q == 0 && a.rows_k == 0)) return ok();
   char* ws = static_cast<char*>(workspace);
   p.delta = reinterpret_cast<float*>(ws + w.delta_off);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
+  p.ws_rows = a.s.thd ? int64_t(a.s.hq) * a.s.total_q : int64_t(a.s.batch) * a.s.hq * a.s.sq;
   p.accumulate = accumulate;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;

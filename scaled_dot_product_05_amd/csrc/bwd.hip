@@ -30,7 +30,7 @@ __device__ __forceinline__ int64_t delta_index(const Shape& s, int b, int h, con
 }
 
 // ----------------------------------------------------------------------------------------
-// pre-pass: Delta_i = dO_i . O_i - dLSE_i
+// pre-pass: Delta_i = dO_i . O_i - dLSE_i, and LSE_i log2(e) as a contiguous array
 // ----------------------------------------------------------------------------------------
 template <int ES, bool BF, int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
@@ -72,6 +72,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
   if (live && c == 0) {
     float dl = p.dlse.ptr ? p.dlse.ptr[b * p.dlse.sb + h * p.dlse.sh + t * p.dlse.ss] : 0.f;
     p.delta[r] = dot - dl;
+    const float l = p.lse.ptr[b * p.lse.sb + h * p.lse.sh + t * p.lse.ss];
+    p.lse2[r] = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
 }
 
@@ -731,15 +733,452 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Pipelined 16-bit backward kernels (16-byte aligned rows, head_dim 64 / 128).
+//
+// Streamed tiles go from HBM straight into LDS (buffer loads with an LDS destination, as
+// in the forward) and stay row-major; their 16-byte chunks are XOR-swizzled by row with
+// swb(), which keeps both access patterns free of bank conflicts: 16-byte row reads of 16
+// consecutive rows (A operands) and transposed 8-byte reads of 4 rows x 64 bytes
+// (ds_read_b64_tr_b16, operands contracted over the tile's rows).
+// ----------------------------------------------------------------------------------------
+template <int CPR>
+__device__ __forceinline__ int swb(int r) {
+  if constexpr (CPR >= 16)
+    return ((r >> 2) & 1) | (((r >> 3) & 1) << 1) | ((r & 1) << 2) | (((r >> 1) & 1) << 3);
+  else if constexpr (CPR == 8)
+    return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  else
+    return (r >> 2) & 3;
+}
+
+// Lane part of the byte offset of a transposed read inside a [rows x CPR chunks] tile:
+// lane 16g + 4c + a supplies row 8h + 4(g/2) + c (plus 16 cc, an immediate), 8-byte half
+// a&1 of chunk 4db + 2(g&1) + a/2.  The swizzle depends on h, so each h has its own offset.
+template <int CPR>
+__device__ __forceinline__ int tr_offset(int lane, int db, int h) {
+  const int g = lane >> 4, c = (lane >> 2) & 3, a = lane & 3;
+  const int row = 8 * h + 4 * (g >> 1) + c;
+  return (row * CPR + ((4 * db + 2 * (g & 1) + (a >> 1)) ^ swb<CPR>(row))) * 16 + (a & 1) * 8;
+}
+
+// dQ.  A workgroup of W waves owns 32 W query rows of one q head (lane = query, as the
+// forward) and streams 32-key tiles:
+//   S^T  = K Q^T     (A: K rows from LDS, B: Q^T in registers)
+//   dP^T = V dO^T    (A: V rows from LDS, B: dO^T in registers)
+//   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T scale log2e - LSE log2e)
+//   dQ^T += K^T dS^T (A: K^T by transposed reads, B: dS^T straight from registers)
+// K and V rings of 4 slots: step t reads K(t), V(t), issues the loads of K(t+3), V(t+3)
+// into the slots step t-1 read, and before its barrier waits for the loads of step t-2,
+// so two steps of loads stay in flight.
+template <bool BF, int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq16p_kernel(BwdParams p) {
+  constexpr int BM = 32 * W, BN = 32, NT = 64 * W;
+  constexpr int CPR = D / 8, TB = BN * D * 2, NDMA = BN * CPR / NT;
+  constexpr int NC = D / 16, NDB = D / 32, NPC = BN / 16;
+  constexpr int NSK = 4, NSV = 4;
+  static_assert(NDMA >= 1 && NPC == 2, "tile split");
+  __shared__ __align__(16) char smem_[(NSK + NSV) * TB];
+  lds_t* const lds = (lds_t*)smem_;
+
+  const Shape& s = p.s;
+  BwdPos w;
+  if (!bwd_decode(s, p.work_q, p.count_q, s.hq, s.sq, BM, true, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hk = w.h / s.group;
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh + g.qrow0 * p.q.ss;
+  const uint16_t* gb = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + w.h * p.dout.sh +
+                       g.qrow0 * p.dout.ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint16_t* dqb = static_cast<uint16_t*>(p.dq.ptr) + w.b * p.dq.sb + w.h * p.dq.sh + g.qrow0 * p.dq.ss;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN, kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  const int qw0 = q0 + wave * 32, qw1 = min(qw0 + 32, g.sq);
+  const int qi = qw0 + l32;
+  int wf0 = 0, wf1 = 0;  // key tiles every row of this wave sees in full
+  if (qw0 < qw1) {
+    const int64_t lo_full = int64_t(qw1 - 1) + g.off + s.lo_rel;
+    const int64_t hi_full = min(int64_t(qw0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
+    const int64_t a = lo_full <= 0 ? 0 : (lo_full + BN - 1) / BN;
+    const int64_t b = hi_full < 0 ? 0 : (hi_full + 1) / BN;
+    wf0 = int(clamp64(a, 0, int64_t(1) << 30));
+    wf1 = int(clamp64(b, wf0, int64_t(1) << 30));
+  }
+
+  // Scores enter exp2 as fma(s, c, -LSE log2e) with c = |scale| log2e; a negative scale
+  // is applied by negating q (exact).  dQ takes the signed scale at the end.
+  const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
+  const uint32_t qsign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
+  uint4 qf[NC], gf[NC];
+  float lse2 = __builtin_inff(), dl = 0.f;
+  {
+    const int qr = min(qi, g.sq - 1);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint4 t = *reinterpret_cast<const uint4*>(qb + qr * p.q.ss + 16 * cc + 8 * hf);
+      qf[cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
+      gf[cc] = *reinterpret_cast<const uint4*>(gb + qr * p.dout.ss + 16 * cc + 8 * hf);
+    }
+    if (qi < g.sq) {
+      const float l = p.lse.ptr[w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss];
+      lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+      dl = p.delta[delta_index(s, w.b, w.h, g, qi)];
+    }
+  }
+
+  // ---- HBM -> LDS: one resource per tensor, a tile is a 32-bit offset ----
+  const int64_t kss = p.k.ss, vss = p.v.ss;
+  const i32x4_t rk = make_rsrc(kb, (int64_t(g.sk) - 1) * kss * 2 + D * 2);
+  const i32x4_t rv = make_rsrc(vb, (int64_t(g.sk) - 1) * vss * 2 + D * 2);
+  const uint32_t kstep = uint32_t(BN * kss * 2), vstep = uint32_t(BN * vss * 2);
+  uint32_t koff_g[NDMA], voff_g[NDMA];
+#pragma unroll
+  for (int u = 0; u < NDMA; ++u) {
+    const int P = (u * W + wave) * 64 + lane;
+    const int row = P / CPR, pos = P % CPR;
+    koff_g[u] = uint32_t(row * kss * 2 + ((pos ^ swb<CPR>(row)) * 16));
+    voff_g[u] = uint32_t(row * vss * 2 + ((pos ^ swb<CPR>(row)) * 16));
+  }
+  auto issue_k = [&](int t, int slot) {
+    const uint32_t o = uint32_t(t) * kstep;
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rk, lds + slot * TB + (u * W + wave) * 1024, koff_g[u] + o);
+  };
+  auto issue_v = [&](int t, int slot) {
+    const uint32_t o = uint32_t(t) * vstep;
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rv, lds + (NSK + slot) * TB + (u * W + wave) * 1024, voff_g[u] + o);
+  };
+
+  // LDS operand offsets (lane part)
+  int ra[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) ra[cc] = (l32 * CPR + ((2 * cc + hf) ^ swb<CPR>(l32))) * 16;
+  int ta[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ta[db][0] = tr_offset<CPR>(lane, db, 0);
+    ta[db][1] = tr_offset<CPR>(lane, db, 1);
+  }
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  // S^T and dP^T of one tile: independent chains, interleaved
+  auto products = [&](int ks, int vs, f32x16_t& st, f32x16_t& dp) {
+    st = zero16();
+    dp = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint4 a = lds_read16(lds + ks * TB + ra[cc]);
+      const uint4 b2 = lds_read16(lds + (NSK + vs) * TB + ra[cc]);
+      st = mfma16<BF>(a, qf[cc], st);
+      dp = mfma16<BF>(b2, gf[cc], dp);
+    }
+  };
+  // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
+  auto grad = [&](int t, const f32x16_t& st, const f32x16_t& dp, uint4(&dsf)[NPC]) {
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = fast_exp2(__builtin_fmaf(st[r], c, -lse2));
+      ds[r] = pr * (dp[r] - dl);
+    }
+    if (t < wf0 || t >= wf1) {
+      asm volatile("" ::: "memory");
+      const int base_rel = t * BN - qi - g.off + 4 * hf;
+      const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rel = base_rel + 8 * (r >> 2) + (r & 3);
+        ds[r] = (rel >= s.lo_rel && rel <= hi_eff) ? ds[r] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < NPC; ++h2)
+      dsf[h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                           pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
+  };
+  auto dq_update = [&](int ks, const uint4(&dsf)[NPC]) {
+#pragma unroll
+    for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_t* base = lds + ks * TB + 16 * cc * CPR * 16;
+        const uint2 lo = read_tr16(base + ta[db][0]), hi = read_tr16(base + ta[db][1]);
+        acc[db] = mfma16<BF>(make_uint4(lo.x, lo.y, hi.x, hi.y), dsf[cc], acc[db]);
+      }
+  };
+
+  const int n = kt1 - kt0;
+  if (n > 0) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      issue_k(kt0 + j, j);
+      issue_v(kt0 + j, j);
+    }
+    vm_wait<4 * NDMA>();
+    lds_barrier();
+  }
+  // step i: tile t = kt0 + i in K and V slot t % 4
+  for (int i = 0; i < n; ++i) {
+    const int ph = i & 3, t = kt0 + i;
+    issue_k(t + 3, (ph + 3) & 3);
+    issue_v(t + 3, (ph + 3) & 3);
+    f32x16_t st, dp;
+    products(ph, ph, st, dp);
+    uint4 dsf[NPC];
+    grad(t, st, dp, dsf);
+    dq_update(ph, dsf);
+    vm_wait<4 * NDMA>();
+    lds_barrier();
+  }
+  vm_wait<0>();  // no load may land in LDS after the workgroup ends
+
+  if (qi < g.sq) {
+    uint16_t* row = dqb + qi * p.dq.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float v[4] = {acc[db][4 * gq], acc[db][4 * gq + 1], acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+        out4_16<BF>(row + db * 32 + 8 * gq + 4 * hf, v, s.scale, true, p.accumulate);
+      }
+  }
+}
+
+// dK, dV.  A workgroup of 2 waves owns 64 keys of one kv head (lane = key) and streams
+// 32-row query tiles of every q head of its group:
+//   S  = Q K^T   (A: Q rows from LDS, B: K^T in registers)
+//   dP = dO V^T  (A: dO rows from LDS, B: V^T in registers)
+//   P = exp2(S scale log2e - LSE log2e),  dS = P (dP - Delta)
+//   dV^T += dO^T P   (A: dO^T by transposed reads, B: P straight from registers)
+//   dK^T += Q^T dS   (A: Q^T by transposed reads, B: dS from registers)
+// Query tiles, with their rows' LSE log2e and Delta from the pre-pass, go to a ring of 4
+// LDS slots, loaded 3 tiles ahead.
+template <bool BF, int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dkdv16p_kernel(BwdParams p) {
+  constexpr int BK = 32 * W, BQ = 32, NT = 64 * W;
+  constexpr int CPR = D / 8, TB = BQ * D * 2, NDMA = BQ * CPR / NT;
+  constexpr int NC = D / 16, NDB = D / 32, NPC = BQ / 16;
+  constexpr int NS = 4, SB = 2 * TB + 256;  // slot: Q tile, dO tile, 32 LSE log2e, 32 Delta
+  constexpr int NL = 2 * NDMA + 1;          // loads per wave per tile
+  static_assert(W == 2 && NDMA >= 1 && NPC == 2, "tile split");
+  __shared__ __align__(16) char smem_[NS * SB];
+  lds_t* const lds = (lds_t*)smem_;
+
+  const Shape& s = p.s;
+  BwdPos w;
+  if (!bwd_decode(s, p.work_k, p.count_k, s.hk, s.sk, BK, false, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int k0 = w.tile * BK;
+  if (k0 >= g.sk) return;
+  const int kend = min(k0 + BK, g.sk);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hk = w.h;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint16_t* dkb = static_cast<uint16_t*>(p.dk.ptr) + w.b * p.dk.sb + hk * p.dk.sh + g.krow0 * p.dk.ss;
+  uint16_t* dvb = static_cast<uint16_t*>(p.dv.ptr) + w.b * p.dv.sb + hk * p.dv.sh + g.krow0 * p.dv.ss;
+
+  int i0, i1;
+  query_range(s, g, k0, kend, i0, i1);
+  const int qt0 = i0 / BQ, qt1 = i1 > i0 ? (i1 + BQ - 1) / BQ : qt0;
+  const int nq = qt1 - qt0, n = s.group * nq;
+  const int kw0 = k0 + wave * 32, kw1 = min(kw0 + 32, g.sk);
+  const int kj = kw0 + l32;
+  // query tiles [wq0, wq1) in which every (query, key) pair of this wave is visible and
+  // every query row exists
+  int wq0 = 0, wq1 = 0;
+  if (kw0 < kw1) {
+    const int64_t lo = int64_t(kw1 - 1) - g.off - s.hi_rel;                      // qbase >= lo
+    const int64_t hi = min(int64_t(kw0) - g.off - s.lo_rel - (BQ - 1), int64_t(g.sq) - BQ);  // qbase <= hi
+    const int64_t a = lo <= 0 ? 0 : (lo + BQ - 1) / BQ;
+    const int64_t b = hi < 0 ? 0 : hi / BQ + 1;
+    wq0 = int(clamp64(a, 0, int64_t(1) << 30));
+    wq1 = int(clamp64(b, wq0, int64_t(1) << 30));
+  }
+
+  // K^T and V^T operands in registers; a negative scale is applied by negating k (exact)
+  const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
+  const uint32_t ksign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
+  uint4 kf[NC], vf[NC];
+  {
+    const int kr = min(kj, g.sk - 1);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint4 t = *reinterpret_cast<const uint4*>(kb + kr * p.k.ss + 16 * cc + 8 * hf);
+      kf[cc] = make_uint4(t.x ^ ksign, t.y ^ ksign, t.z ^ ksign, t.w ^ ksign);
+      vf[cc] = *reinterpret_cast<const uint4*>(vb + kr * p.v.ss + 16 * cc + 8 * hf);
+    }
+  }
+
+  // ---- HBM -> LDS ----
+  const int64_t qss = p.q.ss, gss = p.dout.ss;
+  uint32_t qoff[NDMA], goff[NDMA];
+#pragma unroll
+  for (int u = 0; u < NDMA; ++u) {
+    const int P = (u * W + wave) * 64 + lane;
+    const int row = P / CPR, pos = P % CPR;
+    qoff[u] = uint32_t(row * qss * 2 + ((pos ^ swb<CPR>(row)) * 16));
+    goff[u] = uint32_t(row * gss * 2 + ((pos ^ swb<CPR>(row)) * 16));
+  }
+  // wave 0 loads the tile rows' LSE log2e, wave 1 their Delta (lanes 0..31)
+  const i32x4_t rstat = make_rsrc(wave == 0 ? p.lse2 : p.delta, p.ws_rows * 4);
+  auto issue = [&](int it, int slot) {
+    it = min(it, n - 1);  // past the last item: reload it (never read), keeps wait counts fixed
+    const int h = hk * s.group + it / nq, qbase = (qt0 + it % nq) * BQ;
+    const uint16_t* qh = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * qss;
+    const uint16_t* gh = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh +
+                         g.qrow0 * gss;
+    const i32x4_t rq = make_rsrc(qh, (int64_t(g.sq) - 1) * qss * 2 + D * 2);
+    const i32x4_t rg = make_rsrc(gh, (int64_t(g.sq) - 1) * gss * 2 + D * 2);
+    const uint32_t oq = uint32_t(qbase) * uint32_t(qss * 2), og = uint32_t(qbase) * uint32_t(gss * 2);
+    lds_t* dst = lds + slot * SB;
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rq, dst + (u * W + wave) * 1024, qoff[u] + oq);
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rg, dst + TB + (u * W + wave) * 1024, goff[u] + og);
+    if (lane < 32) dma4(rstat, dst + 2 * TB + wave * 128, uint32_t(delta_index(s, w.b, h, g, qbase + lane)) * 4u);
+  };
+
+  int ra[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) ra[cc] = (l32 * CPR + ((2 * cc + hf) ^ swb<CPR>(l32))) * 16;
+  int ta[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ta[db][0] = tr_offset<CPR>(lane, db, 0);
+    ta[db][1] = tr_offset<CPR>(lane, db, 1);
+  }
+
+  f32x16_t adk[NDB], adv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    adk[i] = zero16();
+    adv[i] = zero16();
+  }
+
+  auto step_compute = [&](int sl, int it) {
+    const lds_t* base = lds + sl * SB;
+    const int qbase = (qt0 + it % nq) * BQ;
+    f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint4 a = lds_read16(base + ra[cc]);
+      const uint4 b2 = lds_read16(base + TB + ra[cc]);
+      st = mfma16<BF>(a, kf[cc], st);
+      dp = mfma16<BF>(b2, vf[cc], dp);
+    }
+    // lane = key; register r holds query 8(r/4) + 4hf + r%4 of the tile
+    float pr[16], ds[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 l4 = lds_read16(base + 2 * TB + (8 * j + 4 * hf) * 4);
+      const uint4 d4 = lds_read16(base + 2 * TB + 128 + (8 * j + 4 * hf) * 4);
+      const float la[4] = {__uint_as_float(l4.x), __uint_as_float(l4.y), __uint_as_float(l4.z), __uint_as_float(l4.w)};
+      const float da[4] = {__uint_as_float(d4.x), __uint_as_float(d4.y), __uint_as_float(d4.z), __uint_as_float(d4.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * j + e;
+        pr[r] = fast_exp2(__builtin_fmaf(st[r], c, -la[e]));
+        ds[r] = pr[r] * (dp[r] - da[e]);
+      }
+    }
+    const int qt = qt0 + it % nq;
+    if (qt < wq0 || qt >= wq1) {
+      asm volatile("" ::: "memory");
+      const int rel0 = kj - qbase - g.off - 4 * hf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = 8 * (r >> 2) + (r & 3);
+        const bool vis = rel0 - qrow >= s.lo_rel && rel0 - qrow <= s.hi_rel && qbase + 4 * hf + qrow < g.sq;
+        pr[r] = vis ? pr[r] : 0.f;
+        ds[r] = vis ? ds[r] : 0.f;
+      }
+    }
+    uint4 pf[NPC], dsf[NPC];
+#pragma unroll
+    for (int h2 = 0; h2 < NPC; ++h2) {
+      pf[h2] = make_uint4(pack2<BF>(pr[8 * h2], pr[8 * h2 + 1]), pack2<BF>(pr[8 * h2 + 2], pr[8 * h2 + 3]),
+                          pack2<BF>(pr[8 * h2 + 4], pr[8 * h2 + 5]), pack2<BF>(pr[8 * h2 + 6], pr[8 * h2 + 7]));
+      dsf[h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                           pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
+    }
+#pragma unroll
+    for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_t* rb = base + 16 * cc * CPR * 16;
+        const uint2 glo = read_tr16(rb + TB + ta[db][0]), ghi = read_tr16(rb + TB + ta[db][1]);
+        adv[db] = mfma16<BF>(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pf[cc], adv[db]);
+        const uint2 qlo = read_tr16(rb + ta[db][0]), qhi = read_tr16(rb + ta[db][1]);
+        adk[db] = mfma16<BF>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsf[cc], adk[db]);
+      }
+  };
+
+  if (n > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    vm_wait<2 * NL>();
+    lds_barrier();
+  }
+  for (int it = 0; it < n; ++it) {
+    const int ph = it & (NS - 1);
+    issue(it + 3, (ph + 3) & (NS - 1));
+    step_compute(ph, it);
+    vm_wait<2 * NL>();
+    lds_barrier();
+  }
+  vm_wait<0>();  // no load may land in LDS after the workgroup ends
+
+  if (kj < g.sk) {
+    uint16_t* krow = dkb + kj * p.dk.ss;
+    uint16_t* vrow = dvb + kj * p.dv.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = db * 32 + 8 * gq + 4 * hf;
+        const float a[4] = {adk[db][4 * gq], adk[db][4 * gq + 1], adk[db][4 * gq + 2], adk[db][4 * gq + 3]};
+        const float b2[4] = {adv[db][4 * gq], adv[db][4 * gq + 1], adv[db][4 * gq + 2], adv[db][4 * gq + 3]};
+        out4_16<BF>(krow + d, a, s.scale, true, p.accumulate);
+        out4_16<BF>(vrow + d, b2, 1.f, true, p.accumulate);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // launches
 // ----------------------------------------------------------------------------------------
 template <class K>
-static hipError_t go(K kernel, const char* name, int64_t blocks, hipStream_t st, const BwdParams& p) {
+static hipError_t go(K kernel, const char* name, int64_t blocks, hipStream_t st, const BwdParams& p,
+                     int threads = kThreads) {
   if (blocks <= 0) return hipSuccess;
   prof_begin(st, name);
-  hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(threads), 0, st, p);
   prof_end(st);
   return hipGetLastError();
+}
+
+// The pipelined kernels read the streamed rows with 16-byte buffer loads at 32-bit offsets
+// and need rows of at least D elements (rows past the sequence end then lie wholly outside
+// the buffer range).
+template <int D>
+static bool pipelined_ok(const BwdParams& p, int64_t rows, int64_t ss_a, int64_t ss_b, int32_t need) {
+  const int64_t ss = ss_a > ss_b ? ss_a : ss_b;
+  return D >= 64 && (p.aligned & need) == need && ss_a >= D && ss_b >= D &&
+         (rows + 4 * 64) * ss * 2 < (int64_t(1) << 31);
 }
 
 template <int ES, bool BF>
@@ -757,8 +1196,22 @@ static hipError_t pre(const BwdParams& p, hipStream_t st) {
 
 template <bool BF, int D>
 static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t bk) {
-  hipError_t e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+  hipError_t e;
+  if constexpr (D >= 64) {
+    static_assert(kBwdK16 == 64, "dK/dV tile keys");
+    if (pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV))
+      e = go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128);
+    else
+      e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+  } else {
+    e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+  }
   if (e != hipSuccess) return e;
+  if constexpr (D >= 64) {
+    static_assert(kBwdQ16 == 64, "dQ tile rows");
+    if (pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ))
+      return go(bwd_dq16p_kernel<BF, D, 2>, "bwd_dq", bq, st, p, 128);
+  }
   return go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
 }
 

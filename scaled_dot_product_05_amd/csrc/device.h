@@ -168,6 +168,13 @@ __device__ __forceinline__ uint4 lds_read16(const lds_t* p) {
   return __builtin_bit_cast(uint4, *(const __attribute__((address_space(3))) u32x4_t*)p);
 }
 
+// 4 bytes per lane straight into LDS: lane i lands at dst + 4 * i (dst wave-uniform);
+// lanes outside the exec mask load nothing.
+__device__ __forceinline__ void dma4(i32x4_t r, lds_t* dst, uint32_t voff) {
+  const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("buffer_load_dword %1, %2, 0 offen lds" : : "{m0}"(d), "v"(voff), "s"(r) : "memory");
+}
+
 // ds_read_b64_tr_b16: lane 16g + 4a + b receives element b of the 8-byte rows addressed by
 // lanes 16g + a + 4c, c = 0..3, as its elements c.
 __device__ __forceinline__ uint2 read_tr16(const lds_t* p) {

@@ -64,6 +64,8 @@ struct BwdParams {
   View q, k, v, o, dout, dq, dk, dv;
   StatView lse, dlse;  // dlse.ptr may be null
   float* delta;        // workspace: Delta_i = dO_i . O_i - dLSE_i, laid out [b][h][row] / [h][t]
+  float* lse2;         // workspace: LSE_i log2(e) (+inf for rows without a visible key), same layout
+  int64_t ws_rows;     // rows of delta and lse2
   const WorkItem* work_q;  // THD: (seq, q tile) list for dQ
   const int32_t* count_q;
   const WorkItem* work_k;  // THD: (seq, k tile) list for dK/dV
