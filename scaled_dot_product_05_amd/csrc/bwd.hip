@@ -86,10 +86,11 @@ struct BwdPos {
 
 __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
                                            const int32_t* count, int heads, int len, int tile_rows,
-                                           bool reverse, BwdPos& w) {
+                                           bool reverse, BwdPos& w, int bid = -1) {
+  if (bid < 0) bid = blockIdx.x;
   if (s.thd) {
-    int item = blockIdx.x / heads;
-    w.h = blockIdx.x % heads;
+    int item = bid / heads;
+    w.h = bid % heads;
     if (item >= *count) return false;
     WorkItem it = work[item];
     w.b = it.seq;
@@ -98,8 +99,8 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
   }
   int bh = s.batch * heads;
   int nt = (len + tile_rows - 1) / tile_rows;
-  int t = blockIdx.x / bh;
-  int r = blockIdx.x % bh;
+  int t = bid / bh;
+  int r = bid % bh;
   w.b = r / heads;
   w.h = r % heads;
   w.tile = reverse ? nt - 1 - t : t;
@@ -770,19 +771,23 @@ __device__ __forceinline__ int tr_offset(int lane, int db, int h) {
 // K and V rings of 4 slots: step t reads K(t), V(t), issues the loads of K(t+3), V(t+3)
 // into the slots step t-1 read, and before its barrier waits for the loads of step t-2,
 // so two steps of loads stay in flight.
+template <int D, int W>
+struct DqP {
+  static constexpr int BN = 32, TB = BN * D * 2, NSK = 4, NSV = 4;
+  static constexpr int LDS = (NSK + NSV) * TB;
+};
+
 template <bool BF, int D, int W>
-__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq16p_kernel(BwdParams p) {
-  constexpr int BM = 32 * W, BN = 32, NT = 64 * W;
-  constexpr int CPR = D / 8, TB = BN * D * 2, NDMA = BN * CPR / NT;
+__device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds, int bid) {
+  constexpr int BM = 32 * W, BN = DqP<D, W>::BN, NT = 64 * W;
+  constexpr int CPR = D / 8, TB = DqP<D, W>::TB, NDMA = BN * CPR / NT;
   constexpr int NC = D / 16, NDB = D / 32, NPC = BN / 16;
-  constexpr int NSK = 4, NSV = 4;
+  constexpr int NSK = DqP<D, W>::NSK, NSV = DqP<D, W>::NSV;
   static_assert(NDMA >= 1 && NPC == 2, "tile split");
-  __shared__ __align__(16) char smem_[(NSK + NSV) * TB];
-  lds_t* const lds = (lds_t*)smem_;
 
   const Shape& s = p.s;
   BwdPos w;
-  if (!bwd_decode(s, p.work_q, p.count_q, s.hq, s.sq, BM, true, w)) return;
+  if (!bwd_decode(s, p.work_q, p.count_q, s.hq, s.sq, BM, true, w, bid)) return;
   const Seq g = seq_of(s, w.b);
   const int q0 = w.tile * BM;
   if (q0 >= g.sq) return;
@@ -964,20 +969,25 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq16p_kernel(BwdParams p) {
 //   dK^T += Q^T dS   (A: Q^T by transposed reads, B: dS from registers)
 // Query tiles, with their rows' LSE log2e and Delta from the pre-pass, go to a ring of 4
 // LDS slots, loaded 3 tiles ahead.
+template <int D, int W>
+struct DkdvP {
+  static constexpr int BQ = 32, TB = BQ * D * 2, NS = 4;
+  static constexpr int SB = 2 * TB + 256;  // slot: Q tile, dO tile, 32 LSE log2e, 32 Delta
+  static constexpr int LDS = NS * SB;
+};
+
 template <bool BF, int D, int W>
-__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dkdv16p_kernel(BwdParams p) {
-  constexpr int BK = 32 * W, BQ = 32, NT = 64 * W;
-  constexpr int CPR = D / 8, TB = BQ * D * 2, NDMA = BQ * CPR / NT;
+__device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid) {
+  constexpr int BK = 32 * W, BQ = DkdvP<D, W>::BQ, NT = 64 * W;
+  constexpr int CPR = D / 8, TB = DkdvP<D, W>::TB, NDMA = BQ * CPR / NT;
   constexpr int NC = D / 16, NDB = D / 32, NPC = BQ / 16;
-  constexpr int NS = 4, SB = 2 * TB + 256;  // slot: Q tile, dO tile, 32 LSE log2e, 32 Delta
-  constexpr int NL = 2 * NDMA + 1;          // loads per wave per tile
+  constexpr int NS = DkdvP<D, W>::NS, SB = DkdvP<D, W>::SB;
+  constexpr int NL = 2 * NDMA + 1;  // loads per wave per tile
   static_assert(W == 2 && NDMA >= 1 && NPC == 2, "tile split");
-  __shared__ __align__(16) char smem_[NS * SB];
-  lds_t* const lds = (lds_t*)smem_;
 
   const Shape& s = p.s;
   BwdPos w;
-  if (!bwd_decode(s, p.work_k, p.count_k, s.hk, s.sk, BK, false, w)) return;
+  if (!bwd_decode(s, p.work_k, p.count_k, s.hk, s.sk, BK, false, w, bid)) return;
   const Seq g = seq_of(s, w.b);
   const int k0 = w.tile * BK;
   if (k0 >= g.sk) return;
@@ -1158,6 +1168,31 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dkdv16p_kernel(BwdParams p)
   }
 }
 
+template <bool BF, int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq16p_kernel(BwdParams p) {
+  __shared__ __align__(16) char smem_[DqP<D, W>::LDS];
+  dq16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
+}
+
+template <bool BF, int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dkdv16p_kernel(BwdParams p) {
+  __shared__ __align__(16) char smem_[DkdvP<D, W>::LDS];
+  dkdv16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
+}
+
+// dK/dV and dQ in one launch: blocks [0, nk) take key tiles, the rest query tiles.  The two
+// halves are independent, so on small problems they fill the chip together instead of one
+// after the other.
+template <bool BF, int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void bwd_fused16p_kernel(BwdParams p, int nk) {
+  constexpr int L = DqP<D, W>::LDS > DkdvP<D, W>::LDS ? DqP<D, W>::LDS : DkdvP<D, W>::LDS;
+  __shared__ __align__(16) char smem_[L];
+  if (int(blockIdx.x) < nk)
+    dkdv16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
+  else
+    dq16p_body<BF, D, W>(p, (lds_t*)smem_, int(blockIdx.x) - nk);
+}
+
 // ----------------------------------------------------------------------------------------
 // launches
 // ----------------------------------------------------------------------------------------
@@ -1196,23 +1231,27 @@ static hipError_t pre(const BwdParams& p, hipStream_t st) {
 
 template <bool BF, int D>
 static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t bk) {
-  hipError_t e;
   if constexpr (D >= 64) {
-    static_assert(kBwdK16 == 64, "dK/dV tile keys");
-    if (pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV))
-      e = go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128);
-    else
-      e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+    static_assert(kBwdQ16 == 64 && kBwdK16 == 64, "tile rows of the pipelined kernels");
+    const bool kv = pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV);
+    const bool q = pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
+    if (kv && q) {
+      if (bk + bq <= 0) return hipSuccess;
+      prof_begin(st, "bwd_main");
+      hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2>), dim3(unsigned(bk + bq)), dim3(128), 0, st, p, int(bk));
+      prof_end(st);
+      return hipGetLastError();
+    }
+    hipError_t e = kv ? go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128)
+                      : go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+    if (e != hipSuccess) return e;
+    return q ? go(bwd_dq16p_kernel<BF, D, 2>, "bwd_dq", bq, st, p, 128)
+             : go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
   } else {
-    e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+    hipError_t e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
+    if (e != hipSuccess) return e;
+    return go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
   }
-  if (e != hipSuccess) return e;
-  if constexpr (D >= 64) {
-    static_assert(kBwdQ16 == 64, "dQ tile rows");
-    if (pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ))
-      return go(bwd_dq16p_kernel<BF, D, 2>, "bwd_dq", bq, st, p, 128);
-  }
-  return go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
 }
 
 template <int D>
