@@ -5,18 +5,20 @@
 // LSE is differentiated, so the backward receives dLSE):
 //   Delta_i = dO_i . O_i - dLSE_i,   P_ij = exp(s_ij - LSE_i),   dP = dO V^T,
 //   dS_ij = P_ij (dP_ij - Delta_i),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
-// Three launches on one stream, no atomics anywhere:
-//   pre   Delta for every query row (streaming, HBM bound);
+// Launches on one stream, no atomics anywhere:
+//   pre   Delta and LSE log2(e) for every query row (streaming, HBM bound);
 //   dq    one workgroup per 64 (16-bit) or 128 (fp32) query rows of a q head, streaming
 //         the key tiles;
 //   dkdv  one workgroup per 64 (16-bit) or 128 (fp32) keys of a kv head, streaming the
 //         query tiles of every q head of its group, so dK and dV of a GQA group are summed
 //         in registers.
-// In 16-bit mode the operands that must be contracted over rows (K in dq; Q and dO in
-// dkdv) are also kept transposed in LDS, written once per tile from the same registers
-// that fill the row-major copy.  16-bit workgroups own 64 rows and split the streamed tile
-// between wave pairs, so small problems still launch enough waves.  fp32 mode uses true fp32 MFMA and reads the transposed
-// operand element-wise from the row-major tile.
+// With 16-byte aligned rows and head_dim 64 or 128, dq and dkdv are the pipelined kernels
+// near the end of this file (streamed tiles loaded straight into LDS, transposed operands
+// read with ds_read_b64_tr_b16) and run as one launch.  Otherwise the register-staged
+// kernels below keep the row-contracted operands (K in dq; Q and dO in dkdv) transposed in
+// LDS, written once per tile from the registers that fill the row-major copy, and split the
+// streamed tile between wave pairs so small problems still launch enough waves.  fp32 mode
+// uses true fp32 MFMA and reads the transposed operand element-wise from the row-major tile.
 #include "device.h"
 #include "launch.h"
 #include "profile.h"
