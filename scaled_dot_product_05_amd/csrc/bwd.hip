@@ -1080,10 +1080,11 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     adv[i] = zero16();
   }
 
-  auto step_compute = [&](int sl, int it) {
+  // S and dP of the tile in slot sl
+  auto products = [&](int sl, f32x16_t& st, f32x16_t& dp) {
     const lds_t* base = lds + sl * SB;
-    const int qbase = (qt0 + it % nq) * BQ;
-    f32x16_t st = zero16(), dp = zero16();
+    st = zero16();
+    dp = zero16();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       const uint4 a = lds_read16(base + ra[cc]);
@@ -1091,6 +1092,11 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       st = mfma16<BF>(a, kf[cc], st);
       dp = mfma16<BF>(b2, vf[cc], dp);
     }
+  };
+  // P, dS and the dV, dK updates of item `it` (slot sl), given its S and dP
+  auto update = [&](int sl, int it, const f32x16_t& st, const f32x16_t& dp) {
+    const lds_t* base = lds + sl * SB;
+    const int qbase = (qt0 + it % nq) * BQ;
     // lane = key; register r holds query 8(r/4) + 4hf + r%4 of the tile
     float pr[16], ds[16];
 #pragma unroll
@@ -1138,19 +1144,29 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       }
   };
 
+  // Step it reads item it (slot it % 4) and item it+1 (the next S and dP, issued before
+  // this item's softmax so the matrix cores run while the VALU works), loads item it+3 and
+  // before its barrier waits for every load but its own, so item it+2 has landed.
+  f32x16_t sa, da, sb, db_;
   if (n > 0) {
     issue(0, 0);
     issue(1, 1);
     issue(2, 2);
-    vm_wait<2 * NL>();
+    vm_wait<NL>();
     lds_barrier();
+    products(0, sa, da);
   }
-  for (int it = 0; it < n; ++it) {
-    const int ph = it & (NS - 1);
+  auto step = [&](int it, int ph, f32x16_t& sc, f32x16_t& dc, f32x16_t& sn, f32x16_t& dn) {
     issue(it + 3, (ph + 3) & (NS - 1));
-    step_compute(ph, it);
-    vm_wait<2 * NL>();
+    products((ph + 1) & (NS - 1), sn, dn);  // past the last item: a reloaded tile, unused
+    update(ph, it, sc, dc);
+    vm_wait<NL>();
     lds_barrier();
+  };
+  for (int it = 0; it < n; ++it) {
+    step(it, it & (NS - 1), sa, da, sb, db_);
+    sa = sb;
+    da = db_;
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
