@@ -770,9 +770,9 @@ __device__ __forceinline__ int tr_offset(int lane, int db, int h) {
 //   dP^T = V dO^T    (A: V rows from LDS, B: dO^T in registers)
 //   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T scale log2e - LSE log2e)
 //   dQ^T += K^T dS^T (A: K^T by transposed reads, B: dS^T straight from registers)
-// K and V rings of 4 slots: step t reads K(t), V(t), issues the loads of K(t+3), V(t+3)
-// into the slots step t-1 read, and before its barrier waits for the loads of step t-2,
-// so two steps of loads stay in flight.
+// K and V rings of 4 slots: step t reads K(t) (transposed, for dQ) and K(t+1), V(t+1) (the
+// next tile's products), and issues the loads of K(t+3), V(t+3) into the slots step t-1
+// read.
 template <int D, int W>
 struct DqP {
   static constexpr int BN = 32, TB = BN * D * 2, NSK = 4, NSV = 4;
@@ -932,21 +932,26 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
       issue_k(kt0 + j, j);
       issue_v(kt0 + j, j);
     }
-    vm_wait<4 * NDMA>();
+    vm_wait<2 * NDMA>();
     lds_barrier();
   }
-  // step i: tile t = kt0 + i in K and V slot t % 4
+  // Step i: tile t = kt0 + i in K and V slot t % 4.  The products of tile t+1 are issued
+  // before tile t's dS, so the matrix cores run while the VALU works; before its barrier a
+  // step waits for every load but its own, so tile t+2 has landed.
+  f32x16_t sa, da, sb, db_;
+  if (n > 0) products(0, 0, sa, da);
   for (int i = 0; i < n; ++i) {
     const int ph = i & 3, t = kt0 + i;
     issue_k(t + 3, (ph + 3) & 3);
     issue_v(t + 3, (ph + 3) & 3);
-    f32x16_t st, dp;
-    products(ph, ph, st, dp);
+    products((ph + 1) & 3, (ph + 1) & 3, sb, db_);  // past the last tile: unused
     uint4 dsf[NPC];
-    grad(t, st, dp, dsf);
+    grad(t, sa, da, dsf);
     dq_update(ph, dsf);
-    vm_wait<4 * NDMA>();
+    vm_wait<2 * NDMA>();
     lds_barrier();
+    sa = sb;
+    da = db_;
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
