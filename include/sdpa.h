@@ -214,6 +214,38 @@ int sdpa_merge_bwd(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* x_a,
                    const sdpa_rowstat_t* dlse_a, const sdpa_tensor_t* dx_b,
                    const sdpa_rowstat_t* dlse_b, void* stream);
 
+/* Context-parallel ring attention, emulated on one GPU ("Add support for cuDNN
+ * FusedAttention + THD + CP", TransformerEngine issue 885: each sequence is split into
+ * 2*cp chunks, rank r holds chunks r and 2*cp-1-r for load balance, K/V chunk pairs move
+ * around a ring, and the ring's result does not depend on the order of its hops).
+ *
+ * `desc` describes the whole sequence: layout BSHD, SBHD or BHSD (not THD), seqlen_q ==
+ * seqlen_k a positive multiple of 2*cp, window (-1,0) (causal) or (-1,-1) (no mask); the
+ * other fields and all tensors are exactly those of sdpa_fwd / sdpa_bwd on the whole
+ * sequence, and the results equal theirs up to rounding.  cp in [1, 64].  hop_order: NULL
+ * (ring order) or a permutation of 0..cp-1; at hop h rank r works on the K/V of rank
+ * (r - hop_order[h]) mod cp.
+ *
+ * Forward: for each rank and each of its q chunks i, every K/V chunk c the hops bring is a
+ * pair that is full (c < i), causal with the diagonal at the chunk start (c == i) or
+ * skipped (c > i; causal only).  Each pair runs sdpa_fwd on the chunk views and its
+ * (O, LSE) is folded into the running result with sdpa_merge_fwd, in hop order.  `lse`
+ * must be given.  Backward: every pair runs sdpa_bwd with the final O and LSE of its rows
+ * (so its P and Delta equal full attention's); each chunk's diagonal pair writes dq, dk,
+ * dv first, every other pair adds to them in hop order.
+ * Workspace: sdpa_cp_workspace_size bytes, caller-owned, used by both calls.  Errors:
+ * validation of the whole problem runs before any launch; an error from a later launch
+ * returns that launch's status (earlier launches of the call may have run). */
+int sdpa_cp_workspace_size(const sdpa_desc_t* desc, int cp, size_t* bytes);
+int sdpa_cp_fwd(const sdpa_desc_t* desc, int cp, const int32_t* hop_order, const sdpa_tensor_t* q,
+                const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* o,
+                const sdpa_rowstat_t* lse, void* workspace, size_t workspace_bytes, void* stream);
+int sdpa_cp_bwd(const sdpa_desc_t* desc, int cp, const int32_t* hop_order, const sdpa_tensor_t* q,
+                const sdpa_tensor_t* k, const sdpa_tensor_t* v, const sdpa_tensor_t* o,
+                const sdpa_rowstat_t* lse, const sdpa_tensor_t* dout, const sdpa_rowstat_t* dlse,
+                const sdpa_tensor_t* dq, const sdpa_tensor_t* dk, const sdpa_tensor_t* dv,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

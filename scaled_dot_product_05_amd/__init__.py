@@ -85,6 +85,12 @@ _SIGNATURES = {
     "sdpa_merge_bwd": ([_P(MergeDesc), _P(Tensor), _P(RowStat), _P(Tensor), _P(RowStat),
                         _P(Tensor), _P(RowStat), _P(Tensor), _P(RowStat), _P(Tensor),
                         _P(RowStat), ctypes.c_void_p], ctypes.c_int),
+    "sdpa_cp_workspace_size": ([_P(Desc), ctypes.c_int, _P(ctypes.c_size_t)], ctypes.c_int),
+    "sdpa_cp_fwd": ([_P(Desc), ctypes.c_int, _P(ctypes.c_int32)] + [_P(Tensor)] * 4
+                    + [_P(RowStat), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "sdpa_cp_bwd": ([_P(Desc), ctypes.c_int, _P(ctypes.c_int32)] + [_P(Tensor)] * 4
+                    + [_P(RowStat), _P(Tensor), _P(RowStat)] + [_P(Tensor)] * 3
+                    + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
 }
 
 _PROFILE_SIGNATURES = {
@@ -264,6 +270,36 @@ def sdpa_merge_bwd(mdesc, x_a, lse_a, x_b, lse_b, g, g_lse, dx_a, dlse_a, dx_b, 
                                 rowstat(dlse_a), tensor(dx_b), rowstat(dlse_b), _stream(stream)))
 
 
+def _order(hop_order):
+    if hop_order is None:
+        return None
+    arr = (ctypes.c_int32 * len(hop_order))(*[int(x) for x in hop_order])
+    return ctypes.cast(arr, _P(ctypes.c_int32)), arr
+
+
+def sdpa_cp_workspace_size(desc: Desc, cp: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().sdpa_cp_workspace_size(ctypes.byref(desc), int(cp), ctypes.byref(n)))
+    return n.value
+
+
+def sdpa_cp_fwd(desc, cp, hop_order, q, k, v, o, lse, workspace=None, stream=None) -> None:
+    wp, wb = _ws(workspace)
+    ho = _order(hop_order)
+    _check(lib().sdpa_cp_fwd(ctypes.byref(desc), int(cp), ho[0] if ho else None, tensor(q),
+                             tensor(k), tensor(v), tensor(o), rowstat(lse), wp, wb, _stream(stream)))
+
+
+def sdpa_cp_bwd(desc, cp, hop_order, q, k, v, o, lse, dout, dlse, dq, dk, dv, workspace=None,
+                stream=None) -> None:
+    wp, wb = _ws(workspace)
+    ho = _order(hop_order)
+    _check(lib().sdpa_cp_bwd(ctypes.byref(desc), int(cp), ho[0] if ho else None, tensor(q),
+                             tensor(k), tensor(v), tensor(o), rowstat(lse), tensor(dout),
+                             rowstat(dlse), tensor(dq), tensor(dk), tensor(dv), wp, wb,
+                             _stream(stream)))
+
+
 # ---------------------------------------------------------------------------------------
 # conveniences: describe a call from the tensors and allocate the outputs (torch.empty)
 # ---------------------------------------------------------------------------------------
@@ -358,6 +394,31 @@ def merge_backward(x_a, lse_a, x_b, lse_b, g, g_lse, layout: str, stream=None):
     dlb = torch.empty_like(lse_b, memory_format=torch.contiguous_format)
     sdpa_merge_bwd(md, x_a, lse_a, x_b, lse_b, g, g_lse, dxa, dla, dxb, dlb, stream)
     return dxa, dla, dxb, dlb
+
+
+def cp_forward(q, k, v, layout: str, softmax_scale: float, window, cp: int, hop_order=None,
+               stream=None):
+    """Run sdpa_cp_fwd (context-parallel ring emulated on one GPU); returns (O, LSE)."""
+    import torch
+    pr = Problem(q, k, layout, softmax_scale, window)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format)
+    l = torch.empty(pr.lse_shape, dtype=torch.float32, device=q.device)
+    ws = torch.empty(sdpa_cp_workspace_size(pr.desc, cp), dtype=torch.uint8, device=q.device)
+    sdpa_cp_fwd(pr.desc, cp, hop_order, q, k, v, o, l, ws, stream)
+    return o, l
+
+
+def cp_backward(q, k, v, o, lse, dout, layout: str, softmax_scale: float, window, cp: int,
+                hop_order=None, dlse=None, stream=None):
+    """Run sdpa_cp_bwd; returns (dQ, dK, dV)."""
+    import torch
+    pr = Problem(q, k, layout, softmax_scale, window)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    ws = torch.empty(sdpa_cp_workspace_size(pr.desc, cp), dtype=torch.uint8, device=q.device)
+    sdpa_cp_bwd(pr.desc, cp, hop_order, q, k, v, o, lse, dout, dlse, dq, dk, dv, ws, stream)
+    return dq, dk, dv
 
 
 def flops(n_visible: int, head_dim: int, backward: bool = False) -> int:

@@ -577,6 +577,12 @@ SchedParams sched_params(const Shape& s, bool q_items, WorkItem* items, int32_t*
 
 }  // namespace
 
+namespace sdpa {
+// Record an error message for sdpa_last_error() from another translation unit.
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+int clear_error() { return ok(); }
+}  // namespace sdpa
+
 extern "C" {
 
 int sdpa_version(void) { return SDPA_VERSION; }

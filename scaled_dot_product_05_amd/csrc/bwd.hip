@@ -784,7 +784,7 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   constexpr int BM = 32 * W, BN = DqP<D, W>::BN, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DqP<D, W>::TB, NDMA = BN * CPR / NT;
   constexpr int NC = D / 16, NDB = D / 32, NPC = BN / 16;
-  constexpr int NSK = DqP<D, W>::NSK, NSV = DqP<D, W>::NSV;
+  constexpr int NSK = DqP<D, W>::NSK;  // K slots; the V slots follow them
   static_assert(NDMA >= 1 && NPC == 2, "tile split");
 
   const Shape& s = p.s;
@@ -1191,14 +1191,15 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
 }
 
+// Second launch bound: waves per SIMD that registers and LDS allow (at D128: one).
 template <bool BF, int D, int W>
-__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dq16p_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dq16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DqP<D, W>::LDS];
   dq16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
 }
 
 template <bool BF, int D, int W>
-__global__ __launch_bounds__(64 * W, 8 / W) void bwd_dkdv16p_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dkdv16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DkdvP<D, W>::LDS];
   dkdv16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
 }
@@ -1207,7 +1208,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void bwd_dkdv16p_kernel(BwdParams p)
 // halves are independent, so on small problems they fill the chip together instead of one
 // after the other.
 template <bool BF, int D, int W>
-__global__ __launch_bounds__(64 * W, 8 / W) void bwd_fused16p_kernel(BwdParams p, int nk) {
+__global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_fused16p_kernel(BwdParams p, int nk) {
   constexpr int L = DqP<D, W>::LDS > DkdvP<D, W>::LDS ? DqP<D, W>::LDS : DkdvP<D, W>::LDS;
   __shared__ __align__(16) char smem_[L];
   if (int(blockIdx.x) < nk)

@@ -113,7 +113,6 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16_kernel(FwdParams p) {
     kf0 = int(clamp64(a, kt0, kt1));
     kf1 = int(clamp64(b, kf0, kt1));
   }
-  const int nf = kf1 - kf0;
 
   const int qw0 = q0 + wave * 32;
   const int qw1 = min(qw0 + 32, g.sq);

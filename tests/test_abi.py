@@ -26,7 +26,7 @@ def header_functions():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = S.lib()
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.exported_symbols())
@@ -181,3 +181,29 @@ def test_merge_validation():
                                                 (40, 40, (-1, -129), 0), (33, 17, (-1, -1), 0)])
 def test_visible_pair_count_matches_the_mask(sq, sk, window, align):
     assert S.n_visible(sq, sk, window, align) == int(window_mask(sq, sk, *window, align).sum())
+
+
+def test_cp_validation_on_host():
+    import torch
+    q = torch.empty(2, 192, 4, 64, dtype=torch.bfloat16)
+    pr = S.Problem(q, q, "bshd", 0.125, (-1, 0))
+    assert S.sdpa_cp_workspace_size(pr.desc, 2) > 0
+    # seqlen 192 is not a multiple of 2 * 5
+    with pytest.raises(S.SdpaError) as e:
+        S.sdpa_cp_workspace_size(pr.desc, 5)
+    assert e.value.args[0] == "SDPA_ERR_SHAPE" or "SHAPE" in str(e.value)
+    # a sliding window is not a ring-decomposable mask here
+    pw = S.Problem(q, q, "bshd", 0.125, (128, 0))
+    with pytest.raises(S.SdpaError):
+        S.sdpa_cp_workspace_size(pw.desc, 2)
+    # THD is not supported by the emulation
+    cu = torch.tensor([0, 96, 192], dtype=torch.int32)
+    pt = S.Problem(q[0], q[0], "thd", 0.125, (-1, 0), cu_seqlens_q=cu, max_seqlen_q=96)
+    with pytest.raises(S.SdpaError):
+        S.sdpa_cp_workspace_size(pt.desc, 2)
+    # hop_order must be a permutation
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 4, 192)
+    ws = torch.empty(S.sdpa_cp_workspace_size(pr.desc, 2), dtype=torch.uint8)
+    with pytest.raises(S.SdpaError):
+        S.sdpa_cp_fwd(pr.desc, 2, [0, 0], q, q, q, o, lse, ws)

@@ -447,3 +447,52 @@ def test_pages_tolerance_context():
         gold = json.load(f)
     assert gold["contiguous_copies"] <= 4e-3 and gold["fixed_scale_0p1"] <= 4e-3
     assert gold["strided_views_wrong"] > 1.0  # the signature of strides read wrongly
+
+
+def test_cp_load_balanced_ring_fold_equals_causal_attention():
+    """"Add support for cuDNN FusedAttention + THD + CP" (TransformerEngine issue 885): a
+    sequence cut into 2*cp chunks, rank r holding chunks r and 2*cp-1-r, K/V chunks visited
+    in any hop order, each (q chunk, kv chunk) pair attended fully (earlier kv chunk),
+    causally (same chunk) or not at all (later chunk), and the partials folded with the LSE
+    merge, is causal attention over the whole sequence, and the fold order does not matter.
+    Gradients: each pair's backward with the final O and LSE sums to the full backward."""
+    rng = np.random.default_rng(885)
+    cp, L, d = 3, 5, 4
+    s = 2 * cp * L
+    q, k, v, g = (rng.standard_normal((1, 2, s, d)) for _ in range(4))
+    scale = 0.7
+    full_o, full_l = oracle.attention_forward(q, k, v, scale, oracle.window_mask(s, s, -1, 0))
+    dq_f, dk_f, dv_f = oracle.attention_backward(q, k, v, g, scale, oracle.window_mask(s, s, -1, 0))
+    sl = lambda c: slice(c * L, (c + 1) * L)
+    for order in ([0, 1, 2], [2, 0, 1]):
+        o = np.zeros_like(full_o)
+        l = np.zeros_like(full_l)
+        for r in range(cp):
+            for i in (r, 2 * cp - 1 - r):
+                acc = None
+                for h in order:
+                    src = (r - h) % cp
+                    for c in sorted((src, 2 * cp - 1 - src)):
+                        if c > i:
+                            continue
+                        m = np.ones((L, L), bool) if c < i else np.tril(np.ones((L, L), bool))
+                        part = oracle.attention_forward(q[:, :, sl(i)], k[:, :, sl(c)], v[:, :, sl(c)], scale, m)
+                        acc = part if acc is None else oracle.merge_forward(*acc, *part)
+                o[:, :, sl(i)], l[:, :, sl(i)] = acc
+        assert np.abs(o - full_o).max() < 1e-12 and np.abs(l - full_l).max() < 1e-12
+    # per-pair backward with the final statistics: P and Delta of full attention
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for i in range(2 * cp):
+        for c in range(i + 1):
+            m = np.ones((L, L), bool) if c < i else np.tril(np.ones((L, L), bool))
+            qi, kc, vc, gi = q[:, :, sl(i)], k[:, :, sl(c)], v[:, :, sl(c)], g[:, :, sl(i)]
+            sc = scale * qi[0] @ kc[0].transpose(0, 2, 1)
+            p = np.where(m, np.exp(sc - full_l[0, :, sl(i), None]), 0.0)
+            delta = (gi[0] * full_o[0, :, sl(i)]).sum(-1)
+            dp = gi[0] @ vc[0].transpose(0, 2, 1)
+            ds = p * (dp - delta[..., None])
+            dq[0, :, sl(i)] += scale * ds @ kc[0]
+            dk[0, :, sl(c)] += scale * ds.transpose(0, 2, 1) @ qi[0]
+            dv[0, :, sl(c)] += p.transpose(0, 2, 1) @ gi[0]
+    for a, b in ((dq, dq_f), (dk, dk_f), (dv, dv_f)):
+        assert np.abs(a - b).max() < 1e-12
