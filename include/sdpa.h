@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SDPA_VERSION 1
+#define SDPA_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum sdpa_status {
@@ -103,7 +103,15 @@ typedef struct sdpa_rowstat {
  *             value, negative ones included, is an offset bound: (-1,-129) keeps only keys
  *             at least 129 behind the query.  A query with no visible key gets O = 0 and
  *             LSE = -inf and contributes no gradient.
- * diag_align  enum sdpa_diag_align. */
+ * diag_align  enum sdpa_diag_align.
+ * cu_seqlens_q_padded / cu_seqlens_k_padded  THD only, optional (NULL: sequences packed
+ *             back to back): DEVICE int32[batch+1], the packed row where each sequence starts
+ *             ("Add support for cuDNN FusedAttention + THD + CP", TransformerEngine issue
+ *             885: THD tensors with padding tokens between sequences).  Sequence b occupies
+ *             rows [padded[b], padded[b] + (cu_seqlens[b+1] - cu_seqlens[b])); the rows after
+ *             it up to padded[b+1] are padding: never read as keys and never written (O, LSE,
+ *             dQ, dK and dV of padding rows keep their contents; dLSE/Delta of them are not
+ *             used).  Entries are clamped to [0, total] on the device. */
 typedef struct sdpa_desc {
   int32_t layout;
   int32_t dtype;
@@ -121,6 +129,8 @@ typedef struct sdpa_desc {
   int32_t window_left;
   int32_t window_right;
   int32_t diag_align;
+  const int32_t* cu_seqlens_q_padded;
+  const int32_t* cu_seqlens_k_padded;
 } sdpa_desc_t;
 
 /* Merge description: rows of x are [layout order] tensors of `heads` heads of head_dim,

@@ -39,16 +39,28 @@ def _seq(t, lo, hi):
     return np.asarray(t[lo:hi], np.float64).transpose(1, 0, 2)[None]
 
 
-def thd_forward(q, k, v, cu_q, cu_k, scale, window=(-1, -1), diag_align=0):
+def _rows(cu, pad, s):
+    """Packed rows of sequence s: [pad[s], pad[s] + len) with len from cu (pad None: cu)."""
+    lo = int(cu[s]) if pad is None else int(pad[s])
+    return lo, lo + int(cu[s + 1]) - int(cu[s])
+
+
+def thd_forward(q, k, v, cu_q, cu_k, scale, window=(-1, -1), diag_align=0, pad_q=None,
+                pad_k=None):
     """Packed varlen forward: every sequence is its own B=1 problem.
 
-    q [T,Hq,D], k,v [Tk,Hk,D]; returns O [T,Hq,D] and LSE [Hq,T].
+    q [T,Hq,D], k,v [Tk,Hk,D]; returns O [T,Hq,D] and LSE [Hq,T].  With pad_q / pad_k
+    ("Add support for cuDNN FusedAttention + THD + CP", TransformerEngine issue 885:
+    cu_seqlens_padded) sequence s starts at packed row pad[s] and the rows after its end are
+    padding: they are not keys, and their O / LSE entries are NaN here (never written).
     """
     q = np.asarray(q, np.float64)
-    o = np.zeros(q.shape)
-    lse = np.full((q.shape[1], q.shape[0]), NEG_INF)
+    padded = pad_q is not None or pad_k is not None
+    o = np.full(q.shape, np.nan) if padded else np.zeros(q.shape)
+    lse = np.full((q.shape[1], q.shape[0]), np.nan if padded else NEG_INF)
     for s in range(len(cu_q) - 1):
-        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        q0, q1 = _rows(cu_q, pad_q, s)
+        k0, k1 = _rows(cu_k, pad_k, s)
         if q1 == q0:
             continue
         os_, ls = windowed_forward(_seq(q, q0, q1), _seq(k, k0, k1), _seq(v, k0, k1), scale,
@@ -58,12 +70,19 @@ def thd_forward(q, k, v, cu_q, cu_k, scale, window=(-1, -1), diag_align=0):
     return o, lse
 
 
-def thd_backward(q, k, v, dout, cu_q, cu_k, scale, window=(-1, -1), diag_align=0, dlse=None):
-    """Packed varlen backward; dlse [Hq,T] or None.  Returns dQ [T,Hq,D], dK, dV [Tk,Hk,D]."""
+def thd_backward(q, k, v, dout, cu_q, cu_k, scale, window=(-1, -1), diag_align=0, dlse=None,
+                 pad_q=None, pad_k=None):
+    """Packed varlen backward; dlse [Hq,T] or None.  Returns dQ [T,Hq,D], dK, dV [Tk,Hk,D]
+    (padding rows NaN when pad_q / pad_k are given)."""
     q, k, v, dout = (np.asarray(t, np.float64) for t in (q, k, v, dout))
-    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    padded = pad_q is not None or pad_k is not None
+    fill = np.nan if padded else 0.0
+    dq, dk, dv = np.full(q.shape, fill), np.full(k.shape, fill), np.full(v.shape, fill)
     for s in range(len(cu_q) - 1):
-        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        q0, q1 = _rows(cu_q, pad_q, s)
+        k0, k1 = _rows(cu_k, pad_k, s)
+        if padded:
+            dq[q0:q1], dk[k0:k1], dv[k0:k1] = 0.0, 0.0, 0.0
         if q1 == q0 or k1 == k0:
             continue
         dl = None if dlse is None else np.asarray(dlse, np.float64)[:, q0:q1][None]

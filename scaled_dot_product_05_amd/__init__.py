@@ -51,7 +51,8 @@ class Desc(ctypes.Structure):
                 ("cu_seqlens_k", ctypes.c_void_p), ("total_q", ctypes.c_int64),
                 ("total_k", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
-                ("diag_align", ctypes.c_int32)]
+                ("diag_align", ctypes.c_int32), ("cu_seqlens_q_padded", ctypes.c_void_p),
+                ("cu_seqlens_k_padded", ctypes.c_void_p)]
 
 
 class MergeDesc(ctypes.Structure):
@@ -163,14 +164,18 @@ def _stream(stream) -> Optional[int]:
 def make_desc(layout: str, dtype: str, batch: int, seqlen_q: int, seqlen_k: int, heads_q: int,
               heads_kv: int, head_dim: int, softmax_scale: float, window=(-1, -1),
               diag_align: str | int = "top_left", cu_seqlens_q=None, cu_seqlens_k=None,
-              total_q: int = 0, total_k: int = 0) -> Desc:
+              total_q: int = 0, total_k: int = 0, cu_seqlens_q_padded=None,
+              cu_seqlens_k_padded=None) -> Desc:
     """Fill a sdpa_desc_t.  cu_seqlens_* are device int32 tensors (THD only)."""
     al = ALIGN[diag_align] if isinstance(diag_align, str) else int(diag_align)
-    cq = ctypes.c_void_p(cu_seqlens_q.data_ptr()) if cu_seqlens_q is not None else None
-    ck = ctypes.c_void_p(cu_seqlens_k.data_ptr()) if cu_seqlens_k is not None else cq
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    cq = ptr(cu_seqlens_q)
+    ck = ptr(cu_seqlens_k) if cu_seqlens_k is not None else cq
+    pq = ptr(cu_seqlens_q_padded)
+    pk = ptr(cu_seqlens_k_padded) if cu_seqlens_k_padded is not None else pq
     return Desc(LAYOUTS[layout], DTYPES[dtype], batch, seqlen_q, seqlen_k, heads_q, heads_kv,
                 head_dim, cq, ck, total_q, total_k, float(softmax_scale), int(window[0]),
-                int(window[1]), al)
+                int(window[1]), al, pq, pk)
 
 
 def make_merge_desc(layout: str, dtype: str, batch: int, seqlen: int, heads: int, head_dim: int,
@@ -309,7 +314,8 @@ class Problem:
 
     def __init__(self, q, k, layout: str, softmax_scale: Optional[float] = None, window=(-1, -1),
                  diag_align="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
-                 max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None):
+                 max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                 cu_seqlens_q_padded=None, cu_seqlens_k_padded=None):
         self.layout = layout
         self.dtype = _dtype_name(q)
         d = q.shape[-1]
@@ -323,7 +329,8 @@ class Problem:
             self.desc = make_desc(layout, self.dtype, b, max_seqlen_q,
                                   max_seqlen_q if max_seqlen_k is None else max_seqlen_k,
                                   q.shape[1], k.shape[1], d, softmax_scale, window, diag_align,
-                                  cu_seqlens_q, ck, q.shape[0], k.shape[0])
+                                  cu_seqlens_q, ck, q.shape[0], k.shape[0], cu_seqlens_q_padded,
+                                  cu_seqlens_k_padded)
             self.lse_shape = (q.shape[1], q.shape[0])
         else:
             bdim, sdim, hdim = {"bshd": (0, 1, 2), "sbhd": (1, 0, 2), "bhsd": (0, 2, 1)}[layout]
@@ -331,16 +338,17 @@ class Problem:
             self.desc = make_desc(layout, self.dtype, b, sq, k.shape[sdim], hq, k.shape[hdim], d,
                                   softmax_scale, window, diag_align)
             self.lse_shape = (b, hq, sq)
-        self.keep = (cu_seqlens_q, cu_seqlens_k)  # device arrays must outlive the calls
+        # device arrays must outlive the calls
+        self.keep = (cu_seqlens_q, cu_seqlens_k, cu_seqlens_q_padded, cu_seqlens_k_padded)
 
 
 def forward(q, k, v, layout: str, softmax_scale: float, window=(-1, -1), diag_align="top_left",
             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            out=None, lse=None, stream=None):
+            out=None, lse=None, stream=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None):
     """Run sdpa_fwd; returns (O, LSE) with O shaped like q and LSE fp32."""
     import torch
     pr = Problem(q, k, layout, softmax_scale, window, diag_align, cu_seqlens_q, cu_seqlens_k,
-                 max_seqlen_q, max_seqlen_k)
+                 max_seqlen_q, max_seqlen_k, cu_seqlens_q_padded, cu_seqlens_k_padded)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     l = torch.empty(pr.lse_shape, dtype=torch.float32, device=q.device) if lse is None else lse
     nws = sdpa_fwd_workspace_size(pr.desc)
@@ -352,11 +360,12 @@ def forward(q, k, v, layout: str, softmax_scale: float, window=(-1, -1), diag_al
 def backward(q, k, v, o, lse, dout, layout: str, softmax_scale: float, window=(-1, -1),
              diag_align="top_left", dlse=None, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
-             accumulate: bool = False, stream=None):
+             accumulate: bool = False, stream=None, cu_seqlens_q_padded=None,
+             cu_seqlens_k_padded=None):
     """Run sdpa_bwd; returns (dQ, dK, dV)."""
     import torch
     pr = Problem(q, k, layout, softmax_scale, window, diag_align, cu_seqlens_q, cu_seqlens_k,
-                 max_seqlen_q, max_seqlen_k)
+                 max_seqlen_q, max_seqlen_k, cu_seqlens_q_padded, cu_seqlens_k_padded)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv

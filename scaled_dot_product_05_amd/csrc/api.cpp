@@ -249,6 +249,8 @@ int check_desc(const sdpa_desc_t* d, Shape* s) {
       return fail(SDPA_ERR_NULL, "THD needs cu_seqlens_q and cu_seqlens_k");
     if (d->total_q < 0 || d->total_k < 0 || d->total_q > INT32_MAX || d->total_k > INT32_MAX)
       return fail(SDPA_ERR_SHAPE, "total_q/total_k out of range");
+  } else if (d->cu_seqlens_q_padded || d->cu_seqlens_k_padded) {
+    return fail(SDPA_ERR_ARG, "cu_seqlens_*_padded are for the THD layout only");
   }
   memset(s, 0, sizeof(*s));
   s->batch = d->batch;
@@ -261,6 +263,8 @@ int check_desc(const sdpa_desc_t* d, Shape* s) {
   s->thd = thd;
   s->cu_q = d->cu_seqlens_q;
   s->cu_k = d->cu_seqlens_k;
+  s->pad_q = thd ? d->cu_seqlens_q_padded : nullptr;
+  s->pad_k = thd ? d->cu_seqlens_k_padded : nullptr;
   s->total_q = thd ? d->total_q : 0;
   s->total_k = thd ? d->total_k : 0;
   s->lo_rel = d->window_left == -1 ? -kUnbounded : clamp_rel(-int64_t(d->window_left));

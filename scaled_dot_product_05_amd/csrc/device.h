@@ -251,10 +251,15 @@ __device__ __forceinline__ Seq seq_of(const Shape& s, int b) {
     int64_t a1 = clamp64(s.cu_q[b + 1], a0, s.total_q);
     int64_t c0 = clamp64(s.cu_k[b], 0, s.total_k);
     int64_t c1 = clamp64(s.cu_k[b + 1], c0, s.total_k);
-    r.qrow0 = a0;
-    r.krow0 = c0;
-    r.sq = int32_t(a1 - a0 < s.sq ? a1 - a0 : s.sq);
-    r.sk = int32_t(c1 - c0 < s.sk ? c1 - c0 : s.sk);
+    // with padding the rows start at the padded offsets; lengths still come from cu_seqlens
+    r.qrow0 = s.pad_q ? clamp64(s.pad_q[b], 0, s.total_q) : a0;
+    r.krow0 = s.pad_k ? clamp64(s.pad_k[b], 0, s.total_k) : c0;
+    int64_t lq = a1 - a0 < s.sq ? a1 - a0 : s.sq;
+    int64_t lk = c1 - c0 < s.sk ? c1 - c0 : s.sk;
+    lq = lq < s.total_q - r.qrow0 ? lq : s.total_q - r.qrow0;
+    lk = lk < s.total_k - r.krow0 ? lk : s.total_k - r.krow0;
+    r.sq = int32_t(lq);
+    r.sk = int32_t(lk);
   } else {
     r.qrow0 = 0;
     r.krow0 = 0;

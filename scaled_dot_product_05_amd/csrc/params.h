@@ -32,6 +32,8 @@ struct Shape {
   int32_t thd;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  const int32_t* pad_q;  // THD with padding: first packed row of each sequence (else null)
+  const int32_t* pad_k;
   int64_t total_q, total_k;
   int32_t lo_rel, hi_rel;
   int32_t bottom_right;

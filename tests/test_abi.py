@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.exported_symbols())
-    assert S.sdpa_version() == 1
+    assert S.sdpa_version() == 2
 
 
 def status_of(fn, *args):

@@ -496,3 +496,32 @@ def test_cp_load_balanced_ring_fold_equals_causal_attention():
             dv[0, :, sl(c)] += p.transpose(0, 2, 1) @ gi[0]
     for a, b in ((dq, dq_f), (dk, dk_f), (dv, dv_f)):
         assert np.abs(a - b).max() < 1e-12
+
+
+def test_thd_padded_rows_equal_compact_rows():
+    """Padded THD ("Add support for cuDNN FusedAttention + THD + CP", TransformerEngine issue
+    885: cu_seqlens_padded): sequence s lives at packed rows [pad[s], pad[s] + len_s); on the
+    compacted tensor the same sequence gives the same rows, and padding rows are never
+    written (NaN in the oracle's outputs), whatever the padding rows of q/k/v hold."""
+    rng = np.random.default_rng(7)
+    lengths, gaps = [5, 0, 3, 7], [2, 1, 0, 3]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    pad = np.concatenate([[0], np.cumsum(np.add(lengths, gaps))]).astype(np.int32)
+    hq, hk, d = 4, 2, 8
+    T, Tp = int(cu[-1]), int(pad[-1])
+    q, k, v, g = (rng.standard_normal((T, h, d)) for h in (hq, hk, hk, hq))
+    rows = np.concatenate([np.arange(pad[s], pad[s] + lengths[s]) for s in range(len(lengths))])
+    def padded(t):
+        out = np.full((Tp,) + t.shape[1:], np.nan)
+        out[rows] = t
+        return out
+    o, l = oracle.thd_forward(q, k, v, cu, cu, 0.5, (-1, 0))
+    op, lp = oracle.thd_forward(padded(q), padded(k), padded(v), cu, cu, 0.5, (-1, 0), pad_q=pad, pad_k=pad)
+    assert np.array_equal(op[rows], o) and np.array_equal(lp[:, rows], l)
+    gap_rows = np.setdiff1d(np.arange(Tp), rows)
+    assert np.isnan(op[gap_rows]).all() and np.isnan(lp[:, gap_rows]).all()
+    grads = oracle.thd_backward(q, k, v, g, cu, cu, 0.5, (-1, 0))
+    gradsp = oracle.thd_backward(padded(q), padded(k), padded(v), padded(g), cu, cu, 0.5, (-1, 0),
+                                 pad_q=pad, pad_k=pad)
+    for a, b in zip(gradsp, grads):
+        assert np.array_equal(a[rows], b) and np.isnan(a[gap_rows]).all()
