@@ -512,11 +512,15 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
       }
     }
   };
-  // Lazy rescaling: the reference max only moves when a tile's max exceeds it by more than
-  // kTau (log2 units), so P <= 2^kTau and the O accumulator is rarely rescaled.
+  // Lazy rescaling: the reference max m_run only moves when a tile's max exceeds it by more
+  // than kTau (log2 units), so the O accumulator is rarely rescaled.  A tile is first
+  // exponentiated against the current m_run with no max taken; the per-lane partial sums,
+  // which are needed anyway, then show whether that was safe: every P is at most its lane's
+  // sum, so a sum <= kSumMax bounds every P by 2^13 (fp16 P stays finite).  Only a lane
+  // whose sum is larger (or not finite), or a row with no reference yet that sees a key,
+  // sends the wave through the max and rescale below and a second exponentiation.
+  constexpr float kSumMax = 8192.f;
   auto softmax_ref = [&](const f32x16_t(&st)[QB][NKB]) {
-    float m_tile[QB];
-    bool any = false;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float mx = kNegInf;
@@ -525,24 +529,20 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[j][k2][r]);
       mx = max_halves(mx);
-      m_tile[j] = mx == kNegInf ? kNegInf : mx * c;
-      any = any || (m_tile[j] > m_run[j] + kTau);
-    }
-    if (__builtin_amdgcn_ballot_w64(any) != 0) {
+      const float m_tile = mx == kNegInf ? kNegInf : mx * c;
+      const bool raise = m_tile > m_run[j] + kTau;
+      const float alpha = raise ? fast_exp2(m_run[j] - m_tile) : 1.f;
+      m_run[j] = raise ? m_tile : m_run[j];
+      l_run[j] *= alpha;
 #pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        const bool raise = m_tile[j] > m_run[j] + kTau;
-        const float alpha = raise ? fast_exp2(m_run[j] - m_tile[j]) : 1.f;
-        m_run[j] = raise ? m_tile[j] : m_run[j];
-        l_run[j] *= alpha;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[j][db][r] *= alpha;
-      }
+        for (int r = 0; r < 16; ++r) acc[j][db][r] *= alpha;
     }
   };
-  auto probs = [&](const f32x16_t(&st)[QB][NKB], uint4(&pf)[QB][NPC]) {
+  // P of the tile against m_run (0 while a row has no reference) and this lane's partial
+  // row sums
+  auto probs = [&](const f32x16_t(&st)[QB][NKB], uint4(&pf)[QB][NPC], float(&ps)[QB]) {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const float m_use = m_run[j] == kNegInf ? 0.f : m_run[j];
@@ -558,8 +558,21 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
         pf[j][cc] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
                                pack2<BF>(e[6], e[7]));
       }
-      l_run[j] += ps0 + ps1;
+      ps[j] = ps0 + ps1;
     }
+  };
+  auto softmax = [&](const f32x16_t(&st)[QB][NKB], uint4(&pf)[QB][NPC]) {
+    float ps[QB];
+    probs(st, pf, ps);
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) bad = bad || (m_run[j] == kNegInf ? ps[j] > 0.f : !(ps[j] <= kSumMax));
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      softmax_ref(st);
+      probs(st, pf, ps);
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) l_run[j] += ps[j];
   };
 
   // Slots: K(t) lives in K slot t % NS, V(t) in V slot t % NS.  Step t reads K(t+1) (the
@@ -590,10 +603,9 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
     issue_k(t + NS, ph);
     issue_v(t + NS - 1, (ph + NS - 1) % NS);
     mask(t, cur);
-    softmax_ref(cur);
     uint4 pf[QB][NPC];
     scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
-    probs(cur, pf);
+    softmax(cur, pf);
     pv(std::integral_constant<int, ph>(), pf);
     vm_wait<2 * (NS - 2) * NDMA>();
     lds_barrier();
