@@ -15,11 +15,13 @@ import numpy as np
 
 from .attention import (NEG_INF, attention_backward, attention_forward, dkdv_cols,
                         dq_rows, forward_rows, merge_backward, merge_forward, window_mask)
+from .block_mask import block_kinds, block_lists
 
 __all__ = [
     "NEG_INF", "window_mask", "attention_forward", "attention_backward", "forward_rows",
     "dq_rows", "dkdv_cols", "merge_forward", "merge_backward", "thd_forward",
-    "thd_backward", "windowed_forward", "windowed_backward",
+    "thd_backward", "windowed_forward", "windowed_backward", "block_kinds", "block_lists",
+    "masked_forward", "masked_backward",
 ]
 
 
@@ -92,3 +94,16 @@ def thd_backward(q, k, v, dout, cu_q, cu_k, scale, window=(-1, -1), diag_align=0
         dk[k0:k1] = b[0].transpose(1, 0, 2)
         dv[k0:k1] = c[0].transpose(1, 0, 2)
     return dq, dk, dv
+
+
+def masked_forward(q, k, v, scale, mask, window=(-1, -1), diag_align=0):
+    """Forward with an element mask (boolean, broadcastable to [B,Hq,Sq,Sk]) ANDed with the
+    (left, right) window: the block-sparse path's result (the block table only decides
+    which blocks need the element test, never which pairs are visible)."""
+    wm = window_mask(q.shape[2], k.shape[2], window[0], window[1], diag_align)
+    return attention_forward(q, k, v, scale, np.asarray(mask, bool) & wm)
+
+
+def masked_backward(q, k, v, dout, scale, mask, window=(-1, -1), diag_align=0, dlse=None):
+    wm = window_mask(q.shape[2], k.shape[2], window[0], window[1], diag_align)
+    return attention_backward(q, k, v, dout, scale, np.asarray(mask, bool) & wm, dlse)

@@ -222,3 +222,67 @@ def target(seed: int = 0, b: int = 8, s: int = 4096, h: int = 8, hk: Optional[in
     """Causal bf16 BSHD self-attention, scale 1/sqrt(D): the long-sequence throughput case."""
     return dense(seed, 6, dtype, "bshd", b, s, s, h, h if hk is None else hk, d,
                  1.0 / math.sqrt(d), window=(-1, 0), with_grad=with_grad, name="target")
+
+
+# ---------------------------------------------------------------------------------------
+# element masks for the block-sparse path (FlexAttention mask_mod predicates of PyTorch
+# issue 135161, and generic structured masks), and their bit packing
+# ---------------------------------------------------------------------------------------
+
+def flex_mask(name: str, sq: int, sk: int, band: int = 128, q_offset: int = 0,
+              doc_lengths=None, seed: int = 0, density: float = 0.5) -> np.ndarray:
+    """Boolean [Sq,Sk] visibility built from a named predicate over (q_idx, kv_idx).
+
+    ``q_offset`` is added to the row index before the predicate (issue 135161's v1 form
+    evaluates its global mask on query rows sliced from ``band`` on, in local indices, so
+    the caller passes the local rows with q_offset = 0 there).
+    Predicates:
+      sliding_window_causal  (q >= kv) & (q - kv <= band)
+      global_causal_v1       q > kv
+      global_causal_v2       (q >= kv) & (q - kv > band)
+      causal                 q >= kv
+      prefix                 kv < band (every query sees the first ``band`` keys)
+      document               q and kv in the same document (``doc_lengths``), causal
+      random_blocks          128x128 blocks drawn empty / full / random bits
+      random                 independent bits with probability ``density``
+    """
+    qi = np.arange(sq)[:, None] + q_offset
+    kj = np.arange(sk)[None, :]
+    if name == "sliding_window_causal":
+        return (qi >= kj) & (qi - kj <= band)
+    if name == "global_causal_v1":
+        return np.broadcast_to(qi > kj, (sq, sk)).copy()
+    if name == "global_causal_v2":
+        return (qi >= kj) & (qi - kj > band)
+    if name == "causal":
+        return np.broadcast_to(qi >= kj, (sq, sk)).copy()
+    if name == "prefix":
+        return np.broadcast_to(kj < band, (sq, sk)).copy()
+    if name == "document":
+        ends = np.cumsum(np.asarray(doc_lengths))
+        dq = np.searchsorted(ends, qi, side="right")
+        dk = np.searchsorted(ends, kj, side="right")
+        return (dq == dk) & (qi >= kj)
+    rng = np.random.default_rng([seed, 9, sq, sk])
+    if name == "random":
+        return rng.random((sq, sk)) < density
+    if name == "random_blocks":
+        nqb, nkb = -(-sq // 128), -(-sk // 128)
+        kind = rng.integers(0, 3, size=(nqb, nkb))  # 0 empty, 1 full, 2 random bits
+        bits = rng.random((nqb * 128, nkb * 128)) < density
+        full = np.kron(kind == 1, np.ones((128, 128), bool))
+        part = np.kron(kind == 2, np.ones((128, 128), bool)) & bits
+        return (full | part)[:sq, :sk]
+    raise ValueError(f"unknown mask predicate {name!r}")
+
+
+def pack_mask(mask: np.ndarray) -> np.ndarray:
+    """Pack boolean [..., Sq, Sk] into uint64 [..., Sq, ceil(Sk/64)]: bit j of word w of row
+    i is key 64w+j (little-endian bit order; keys past Sk are 0)."""
+    mask = np.asarray(mask, dtype=bool)
+    sk = mask.shape[-1]
+    words = -(-sk // 64)
+    pad = np.zeros(mask.shape[:-1] + (words * 64,), dtype=bool)
+    pad[..., :sk] = mask
+    by = np.packbits(pad, axis=-1, bitorder="little")
+    return np.ascontiguousarray(by).view("<u8").reshape(mask.shape[:-1] + (words,))

@@ -525,3 +525,139 @@ def test_thd_padded_rows_equal_compact_rows():
                                  pad_q=pad, pad_k=pad)
     for a, b in zip(gradsp, grads):
         assert np.array_equal(a[rows], b) and np.isnan(a[gap_rows]).all()
+
+
+# ---------------------------------------------------------------------------------------
+# block-sparse masks (FlexAttention BlockMask model, issue 135161's create_block_mask)
+# ---------------------------------------------------------------------------------------
+
+import synth  # noqa: E402  (input generators; no attention arithmetic)
+from oracle import block_kinds, block_lists  # noqa: E402
+from oracle.block_mask import EMPTY, FULL, PARTIAL  # noqa: E402
+
+
+@pytest.mark.parametrize("s", [512, 300])
+def test_block_kinds_causal_closed_form(s):
+    # q >= kv: a block row qb sees every key of earlier block columns, its own diagonal
+    # block in part, and nothing after it (also with a ragged last block).
+    k = block_kinds(synth.flex_mask("causal", s, s))
+    n = -(-s // 128)
+    want = np.array([[FULL if kb < qb else PARTIAL if kb == qb else EMPTY for kb in range(n)]
+                     for qb in range(n)])
+    assert (k == want).all()
+
+
+@pytest.mark.parametrize("band", [128, 256])
+def test_block_kinds_sliding_window_closed_form(band):
+    # (q >= kv) & (q - kv <= band): over blocks qb, kb the differences q - kv span
+    # 128 (qb - kb) + [-127, 127]; the block is full when that span lies in [0, band], empty
+    # when it misses [0, band], partial otherwise.
+    s = 768
+    k = block_kinds(synth.flex_mask("sliding_window_causal", s, s, band=band))
+    n = s // 128
+    for qb in range(n):
+        for kb in range(n):
+            lo, hi = 128 * (qb - kb) - 127, 128 * (qb - kb) + 127
+            want = FULL if lo >= 0 and hi <= band else EMPTY if hi < 0 or lo > band else PARTIAL
+            assert k[qb, kb] == want, (qb, kb)
+
+
+@pytest.mark.parametrize("name,sq,sk", [("random_blocks", 640, 520), ("random", 200, 330),
+                                        ("document", 700, 700), ("prefix", 300, 600)])
+def test_block_table_covers_the_mask(name, sq, sk):
+    # every visible pair lies in a listed block; a full block has every pair visible, an
+    # empty one none; rows and columns list the same blocks, in increasing order
+    m = synth.flex_mask(name, sq, sk, band=200, doc_lengths=[100, 250, 350], seed=3)
+    kinds = block_kinds(m)
+    kvc, kvl, qc, ql = block_lists(kinds)
+    nqb, nkb = kinds.shape
+    listed = np.zeros((nqb, nkb), np.int32) - 1
+    for qb in range(nqb):
+        ent = kvl[qb, :kvc[qb]]
+        assert (np.diff(ent // 2) > 0).all()
+        for e in ent:
+            listed[qb, e // 2] = e % 2
+        assert (kvl[qb, kvc[qb]:] == -1).all()
+    for kb in range(nkb):
+        ent = ql[kb, :qc[kb]]
+        assert (np.diff(ent // 2) > 0).all()
+        for e in ent:
+            assert listed[e // 2, kb] == e % 2
+    assert qc.sum() == kvc.sum()
+    for qb in range(nqb):
+        for kb in range(nkb):
+            t = m[qb * 128:(qb + 1) * 128, kb * 128:(kb + 1) * 128]
+            if listed[qb, kb] == -1:
+                assert not t.any()
+            elif listed[qb, kb] == 0:
+                assert t.all()
+            else:
+                assert t.any() and not t.all()
+
+
+def _blockwise_forward(q, k, v, scale, mask):
+    """Attention that visits only the listed blocks of each block row, testing the element
+    mask only in partial blocks, with an online (running max / sum) softmax in fp64."""
+    kinds = block_kinds(mask)
+    kvc, kvl, _, _ = block_lists(kinds)
+    sq, d = q.shape
+    o = np.zeros((sq, d))
+    lse = np.full(sq, -np.inf)
+    for qb in range(kinds.shape[0]):
+        rows = slice(qb * 128, min((qb + 1) * 128, sq))
+        m = np.full(rows.stop - rows.start, -np.inf)
+        l = np.zeros_like(m)
+        acc = np.zeros((rows.stop - rows.start, d))
+        for e in kvl[qb, :kvc[qb]]:
+            cols = slice((e // 2) * 128, min((e // 2 + 1) * 128, k.shape[0]))
+            s = scale * q[rows] @ k[cols].T
+            if e % 2:
+                s = np.where(mask[rows, cols], s, -np.inf)
+            mn = np.maximum(m, s.max(axis=1))
+            safe = np.where(np.isfinite(mn), mn, 0.0)
+            a = np.exp(m - safe)
+            p = np.exp(s - safe[:, None])
+            l = l * a + p.sum(axis=1)
+            acc = acc * a[:, None] + p @ v[cols]
+            m = mn
+        ok = l > 0
+        o[rows] = np.where(ok[:, None], acc / np.where(ok, l, 1.0)[:, None], 0.0)
+        lse[rows] = np.where(ok, m + np.log(np.where(ok, l, 1.0)), -np.inf)
+    return o, lse
+
+
+@pytest.mark.parametrize("name", ["random_blocks", "document", "global_causal_v2"])
+def test_blockwise_traversal_equals_masked_attention(name):
+    # skipping empty blocks and not testing full ones changes nothing: the block-sparse
+    # result is the plain masked attention (PyTorch float64 SDPA with the boolean mask)
+    sq, sk, d = 300, 400, 8
+    m = synth.flex_mask(name, sq, sk, band=100, doc_lengths=[90, 150, 160], seed=5)
+    q, k, v = rnd(140, sq, d), rnd(141, sk, d), rnd(142, sk, d)
+    o, lse = _blockwise_forward(q, k, v, 0.3, m)
+    ref = torch_sdpa(q[None, None], k[None, None], v[None, None], 0.3, m[None, None]).numpy()[0, 0]
+    rows = m.any(axis=1)
+    assert np.abs(o[rows] - ref[rows]).max() < 1e-12
+    assert (o[~rows] == 0).all() and np.isneginf(lse[~rows]).all()
+    oo, ol = oracle.masked_forward(q[None, None], k[None, None], v[None, None], 0.3, m)
+    assert np.abs(oo[0, 0] - o).max() < 1e-12
+    assert np.abs(ol[0, 0][rows] - lse[rows]).max() < 1e-12
+
+
+def test_flex_predicates_equal_their_windows():
+    # issue 135161's predicates as element masks: sliding_window_causal = window (band, 0),
+    # global_causal_v2 = window (-1, -(band + 1)); v1 on rows sliced from `band` on
+    # (local index, keys absolute) = v2's rows from `band` on
+    s, band = 512, 128
+    assert (synth.flex_mask("sliding_window_causal", s, s, band) == window_mask(s, s, band, 0)).all()
+    assert (synth.flex_mask("global_causal_v2", s, s, band) == window_mask(s, s, -1, -(band + 1))).all()
+    v1 = synth.flex_mask("global_causal_v1", s - band, s)
+    assert (v1 == window_mask(s - band, s, -1, -(band + 1), diag_align=1)).all()
+
+
+def test_pack_mask_bit_order():
+    m = np.zeros((3, 130), bool)
+    m[0, 0] = m[1, 63] = m[1, 64] = m[2, 129] = True
+    b = synth.pack_mask(m)
+    assert b.shape == (3, 3) and b.dtype == np.uint64
+    assert int(b[0, 0]) == 1 and int(b[1, 0]) == 1 << 63 and int(b[1, 1]) == 1
+    assert int(b[2, 2]) == 2 and int(b[2, 0]) == 0
