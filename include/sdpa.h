@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SDPA_VERSION 2
+#define SDPA_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum sdpa_status {
@@ -111,7 +111,51 @@ typedef struct sdpa_rowstat {
  *             rows [padded[b], padded[b] + (cu_seqlens[b+1] - cu_seqlens[b])); the rows after
  *             it up to padded[b+1] are padding: never read as keys and never written (O, LSE,
  *             dQ, dK and dV of padding rows keep their contents; dLSE/Delta of them are not
- *             used).  Entries are clamped to [0, total] on the device. */
+ *             used).  Entries are clamped to [0, total] on the device.
+ * block_mask  optional (NULL: none): a block-sparse element mask, see sdpa_block_mask_t.
+ *             Key j is then visible to query i iff the window admits it AND the mask bit
+ *             (i, j) is set.  BSHD, SBHD and BHSD only. */
+/* Block-sparse mask (FlexAttention's BlockMask model: "Significant Accuracy Difference
+ * between Compiled and Eager Flex Attention", PyTorch issue 135161, builds its masks with
+ * create_block_mask from predicates over (q_idx, kv_idx) and passes them as block_mask=).
+ * The (seqlen_q, seqlen_k) plane is cut into SDPA_MASK_BLOCK x SDPA_MASK_BLOCK blocks.  A
+ * block with no visible pair is skipped, a block whose every pair is visible is computed
+ * without an element test, any other block tests the element bits.  The result equals plain
+ * attention under the element mask; the block table only saves work.
+ *
+ * batch, heads  extents of the mask: 1 (one mask for every batch entry / every q head) or
+ *               desc->batch / desc->heads_q.  Plane (b, h) of the mask is
+ *               (batch == 1 ? 0 : b) * heads + (heads == 1 ? 0 : h).
+ * bits          DEVICE uint64 [batch][heads][seqlen_q][words], words = ceil(seqlen_k / 64),
+ *               rows contiguous: bit j of word w of row i set <=> key 64 w + j is visible to
+ *               query i.  Bits of keys >= seqlen_k are ignored.  Written by the caller.
+ * kv_count      DEVICE int32 [batch][heads][nqb], nqb = ceil(seqlen_q / SDPA_MASK_BLOCK).
+ * kv_list       DEVICE int32 [batch][heads][nqb][nkb], nkb = ceil(seqlen_k / SDPA_MASK_BLOCK):
+ *               row qb lists, in increasing kb, 2 kb + 1 for each partial block and 2 kb for
+ *               each full block; entries past kv_count are unspecified.
+ * q_count       DEVICE int32 [batch][heads][nkb].
+ * q_list        DEVICE int32 [batch][heads][nkb][nqb]: the same blocks by column, in
+ *               increasing qb (2 qb + partial).
+ * The four table arrays are written by sdpa_block_mask_build from `bits` and read by
+ * sdpa_fwd / sdpa_bwd; all five buffers belong to the caller.  The attention calls trust
+ * the table: it must have been built from these bits for the same seqlen_q / seqlen_k, on
+ * the same stream (or after it).  Block-list entries are clamped to the plane on the device.
+ * Limits (ERR_UNSUPPORTED otherwise): seqlen_q and seqlen_k at most 512 blocks (65536);
+ * fp16/bf16 need 16-byte aligned rows of q, k, v, o (and dO, dq, dk, dv for the backward)
+ * with k/v (and q/dO) row strides >= head_dim; the fp16/bf16 backward needs head_dim >= 64
+ * and, for per-head masks, (heads_q / heads_kv) * ceil(seqlen_q / 128) <= 512.  fp32 takes
+ * any strides.  Not with sdpa_cp_fwd / sdpa_cp_bwd. */
+#define SDPA_MASK_BLOCK 128
+typedef struct sdpa_block_mask {
+  int32_t batch;
+  int32_t heads;
+  const uint64_t* bits;
+  int32_t* kv_count;
+  int32_t* kv_list;
+  int32_t* q_count;
+  int32_t* q_list;
+} sdpa_block_mask_t;
+
 typedef struct sdpa_desc {
   int32_t layout;
   int32_t dtype;
@@ -131,6 +175,7 @@ typedef struct sdpa_desc {
   int32_t diag_align;
   const int32_t* cu_seqlens_q_padded;
   const int32_t* cu_seqlens_k_padded;
+  const sdpa_block_mask_t* block_mask;
 } sdpa_desc_t;
 
 /* Merge description: rows of x are [layout order] tensors of `heads` heads of head_dim,
@@ -190,6 +235,14 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
              const sdpa_tensor_t* dout, const sdpa_rowstat_t* dlse, const sdpa_tensor_t* dq,
              const sdpa_tensor_t* dk, const sdpa_tensor_t* dv, int accumulate, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/* Builds the block table of `mask` (kv_count, kv_list, q_count, q_list) from its bits on
+ * `stream`: every block of the (seqlen_q, seqlen_k) plane is classified over its pairs
+ * inside the plane (the last block row and column may be short).  Asynchronous; reads only
+ * bits, writes only the four table arrays.  Errors: NULL pointers (ERR_NULL), batch or heads
+ * < 1, seqlen_q or seqlen_k < 1 or > 2^28 - 1 (ERR_SHAPE). */
+int sdpa_block_mask_build(const sdpa_block_mask_t* mask, int32_t seqlen_q, int32_t seqlen_k,
+                          void* stream);
 
 /* Host-only dry runs of the merge calls. */
 int sdpa_merge_fwd_validate(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* x_a,

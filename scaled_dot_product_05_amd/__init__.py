@@ -43,6 +43,13 @@ class RowStat(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("stride", ctypes.c_int64 * 3)]
 
 
+class BlockMaskDesc(ctypes.Structure):
+    """sdpa_block_mask_t: element bits and the block table built from them (device arrays)."""
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("bits", ctypes.c_void_p),
+                ("kv_count", ctypes.c_void_p), ("kv_list", ctypes.c_void_p),
+                ("q_count", ctypes.c_void_p), ("q_list", ctypes.c_void_p)]
+
+
 class Desc(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
@@ -52,7 +59,7 @@ class Desc(ctypes.Structure):
                 ("total_k", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("diag_align", ctypes.c_int32), ("cu_seqlens_q_padded", ctypes.c_void_p),
-                ("cu_seqlens_k_padded", ctypes.c_void_p)]
+                ("cu_seqlens_k_padded", ctypes.c_void_p), ("block_mask", ctypes.c_void_p)]
 
 
 class MergeDesc(ctypes.Structure):
@@ -86,6 +93,8 @@ _SIGNATURES = {
     "sdpa_merge_bwd": ([_P(MergeDesc), _P(Tensor), _P(RowStat), _P(Tensor), _P(RowStat),
                         _P(Tensor), _P(RowStat), _P(Tensor), _P(RowStat), _P(Tensor),
                         _P(RowStat), ctypes.c_void_p], ctypes.c_int),
+    "sdpa_block_mask_build": ([_P(BlockMaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p],
+                              ctypes.c_int),
     "sdpa_cp_workspace_size": ([_P(Desc), ctypes.c_int, _P(ctypes.c_size_t)], ctypes.c_int),
     "sdpa_cp_fwd": ([_P(Desc), ctypes.c_int, _P(ctypes.c_int32)] + [_P(Tensor)] * 4
                     + [_P(RowStat), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
@@ -165,17 +174,19 @@ def make_desc(layout: str, dtype: str, batch: int, seqlen_q: int, seqlen_k: int,
               heads_kv: int, head_dim: int, softmax_scale: float, window=(-1, -1),
               diag_align: str | int = "top_left", cu_seqlens_q=None, cu_seqlens_k=None,
               total_q: int = 0, total_k: int = 0, cu_seqlens_q_padded=None,
-              cu_seqlens_k_padded=None) -> Desc:
-    """Fill a sdpa_desc_t.  cu_seqlens_* are device int32 tensors (THD only)."""
+              cu_seqlens_k_padded=None, block_mask=None) -> Desc:
+    """Fill a sdpa_desc_t.  cu_seqlens_* are device int32 tensors (THD only); block_mask a
+    BlockMask (kept alive by the caller)."""
     al = ALIGN[diag_align] if isinstance(diag_align, str) else int(diag_align)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
     cq = ptr(cu_seqlens_q)
     ck = ptr(cu_seqlens_k) if cu_seqlens_k is not None else cq
     pq = ptr(cu_seqlens_q_padded)
     pk = ptr(cu_seqlens_k_padded) if cu_seqlens_k_padded is not None else pq
+    bm = ctypes.cast(ctypes.pointer(block_mask.desc), ctypes.c_void_p) if block_mask is not None else None
     return Desc(LAYOUTS[layout], DTYPES[dtype], batch, seqlen_q, seqlen_k, heads_q, heads_kv,
                 head_dim, cq, ck, total_q, total_k, float(softmax_scale), int(window[0]),
-                int(window[1]), al, pq, pk)
+                int(window[1]), al, pq, pk, bm)
 
 
 def make_merge_desc(layout: str, dtype: str, batch: int, seqlen: int, heads: int, head_dim: int,
@@ -275,6 +286,41 @@ def sdpa_merge_bwd(mdesc, x_a, lse_a, x_b, lse_b, g, g_lse, dx_a, dlse_a, dx_b, 
                                 rowstat(dlse_a), tensor(dx_b), rowstat(dlse_b), _stream(stream)))
 
 
+def sdpa_block_mask_build(mdesc: BlockMaskDesc, seqlen_q: int, seqlen_k: int, stream=None) -> None:
+    _check(lib().sdpa_block_mask_build(ctypes.byref(mdesc), int(seqlen_q), int(seqlen_k),
+                                       _stream(stream)))
+
+
+class BlockMask:
+    """A block-sparse mask on the device: the caller's element bits (uint64
+    [batch, heads, Sq, ceil(Sk/64)], bit j of word w of row i = key 64w+j visible to query
+    i; batch / heads may be 1 to share) and the block table sdpa_block_mask_build writes from
+    them into arrays allocated here."""
+
+    BLOCK = 128
+
+    def __init__(self, bits, seqlen_q: int, seqlen_k: int, stream=None):
+        import torch
+        if bits.dtype not in (torch.int64, torch.uint64) or bits.dim() != 4:
+            raise ValueError("bits must be a 4-D int64/uint64 tensor [batch, heads, Sq, words]")
+        nb, nh = bits.shape[0], bits.shape[1]
+        words = (seqlen_k + 63) // 64
+        if tuple(bits.shape[2:]) != (seqlen_q, words) or not bits.is_contiguous():
+            raise ValueError(f"bits must be contiguous [.., {seqlen_q}, {words}]")
+        nqb, nkb = -(-seqlen_q // self.BLOCK), -(-seqlen_k // self.BLOCK)
+        dev = bits.device
+        self.bits = bits
+        self.kv_count = torch.empty((nb, nh, nqb), dtype=torch.int32, device=dev)
+        self.kv_list = torch.empty((nb, nh, nqb, nkb), dtype=torch.int32, device=dev)
+        self.q_count = torch.empty((nb, nh, nkb), dtype=torch.int32, device=dev)
+        self.q_list = torch.empty((nb, nh, nkb, nqb), dtype=torch.int32, device=dev)
+        self.seqlen_q, self.seqlen_k = seqlen_q, seqlen_k
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.desc = BlockMaskDesc(nb, nh, ptr(bits), ptr(self.kv_count), ptr(self.kv_list),
+                                  ptr(self.q_count), ptr(self.q_list))
+        sdpa_block_mask_build(self.desc, seqlen_q, seqlen_k, stream)
+
+
 def _order(hop_order):
     if hop_order is None:
         return None
@@ -315,7 +361,7 @@ class Problem:
     def __init__(self, q, k, layout: str, softmax_scale: Optional[float] = None, window=(-1, -1),
                  diag_align="top_left", cu_seqlens_q=None, cu_seqlens_k=None,
                  max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-                 cu_seqlens_q_padded=None, cu_seqlens_k_padded=None):
+                 cu_seqlens_q_padded=None, cu_seqlens_k_padded=None, block_mask=None):
         self.layout = layout
         self.dtype = _dtype_name(q)
         d = q.shape[-1]
@@ -336,19 +382,21 @@ class Problem:
             bdim, sdim, hdim = {"bshd": (0, 1, 2), "sbhd": (1, 0, 2), "bhsd": (0, 2, 1)}[layout]
             b, sq, hq = q.shape[bdim], q.shape[sdim], q.shape[hdim]
             self.desc = make_desc(layout, self.dtype, b, sq, k.shape[sdim], hq, k.shape[hdim], d,
-                                  softmax_scale, window, diag_align)
+                                  softmax_scale, window, diag_align, block_mask=block_mask)
             self.lse_shape = (b, hq, sq)
         # device arrays must outlive the calls
-        self.keep = (cu_seqlens_q, cu_seqlens_k, cu_seqlens_q_padded, cu_seqlens_k_padded)
+        self.keep = (cu_seqlens_q, cu_seqlens_k, cu_seqlens_q_padded, cu_seqlens_k_padded,
+                     block_mask)
 
 
 def forward(q, k, v, layout: str, softmax_scale: float, window=(-1, -1), diag_align="top_left",
             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            out=None, lse=None, stream=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None):
+            out=None, lse=None, stream=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
+            block_mask=None):
     """Run sdpa_fwd; returns (O, LSE) with O shaped like q and LSE fp32."""
     import torch
     pr = Problem(q, k, layout, softmax_scale, window, diag_align, cu_seqlens_q, cu_seqlens_k,
-                 max_seqlen_q, max_seqlen_k, cu_seqlens_q_padded, cu_seqlens_k_padded)
+                 max_seqlen_q, max_seqlen_k, cu_seqlens_q_padded, cu_seqlens_k_padded, block_mask)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     l = torch.empty(pr.lse_shape, dtype=torch.float32, device=q.device) if lse is None else lse
     nws = sdpa_fwd_workspace_size(pr.desc)
@@ -361,11 +409,11 @@ def backward(q, k, v, o, lse, dout, layout: str, softmax_scale: float, window=(-
              diag_align="top_left", dlse=None, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
              accumulate: bool = False, stream=None, cu_seqlens_q_padded=None,
-             cu_seqlens_k_padded=None):
+             cu_seqlens_k_padded=None, block_mask=None):
     """Run sdpa_bwd; returns (dQ, dK, dV)."""
     import torch
     pr = Problem(q, k, layout, softmax_scale, window, diag_align, cu_seqlens_q, cu_seqlens_k,
-                 max_seqlen_q, max_seqlen_k, cu_seqlens_q_padded, cu_seqlens_k_padded)
+                 max_seqlen_q, max_seqlen_k, cu_seqlens_q_padded, cu_seqlens_k_padded, block_mask)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv

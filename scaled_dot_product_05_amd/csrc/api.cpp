@@ -252,7 +252,32 @@ int check_desc(const sdpa_desc_t* d, Shape* s) {
   } else if (d->cu_seqlens_q_padded || d->cu_seqlens_k_padded) {
     return fail(SDPA_ERR_ARG, "cu_seqlens_*_padded are for the THD layout only");
   }
+  const sdpa_block_mask_t* m = d->block_mask;
+  if (m) {
+    if (thd) return fail(SDPA_ERR_UNSUPPORTED, "block_mask is for the BSHD, SBHD and BHSD layouts");
+    if (!m->bits || !m->kv_count || !m->kv_list || !m->q_count || !m->q_list)
+      return fail(SDPA_ERR_NULL, "block_mask has a NULL array");
+    if ((m->batch != 1 && m->batch != d->batch) || (m->heads != 1 && m->heads != d->heads_q))
+      return fail(SDPA_ERR_SHAPE, "block_mask batch=%d heads=%d (1 or batch=%d / heads_q=%d)",
+                  m->batch, m->heads, d->batch, d->heads_q);
+    if ((d->seqlen_k + kMaskBlock - 1) / kMaskBlock > kMaskMaxList ||
+        (d->seqlen_q + kMaskBlock - 1) / kMaskBlock > kMaskMaxList)
+      return fail(SDPA_ERR_UNSUPPORTED, "block_mask with seqlen_q %d / seqlen_k %d above %d",
+                  d->seqlen_q, d->seqlen_k, kMaskMaxList * kMaskBlock);
+  }
   memset(s, 0, sizeof(*s));
+  if (m) {
+    s->bm.bits = m->bits;
+    s->bm.kv_count = m->kv_count;
+    s->bm.kv_list = m->kv_list;
+    s->bm.q_count = m->q_count;
+    s->bm.q_list = m->q_list;
+    s->bm.nb = m->batch;
+    s->bm.nh = m->heads;
+    s->bm.nqb = (d->seqlen_q + kMaskBlock - 1) / kMaskBlock;
+    s->bm.nkb = (d->seqlen_k + kMaskBlock - 1) / kMaskBlock;
+    s->bm.words = (d->seqlen_k + 63) / 64;
+  }
   s->batch = d->batch;
   s->sq = d->seqlen_q;
   s->sk = d->seqlen_k;
@@ -395,6 +420,10 @@ int fwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
   if (!has_lse) p->lse.ptr = nullptr;
   p->aligned = (aligned16(nq) ? kAlQ : 0) | (aligned16(nk) ? kAlK : 0) |
                (aligned16(nv) ? kAlV : 0) | (aligned16(no) ? kAlO : 0);
+  if (p->s.bm.bits && !fwd_block_mask_ok(*p, DType(a->dtype)))
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "block_mask needs 16-byte aligned q/k/v/o rows with k/v row strides >= head_dim "
+                "for 16-bit inputs");
   return SDPA_OK;
 }
 
@@ -437,6 +466,10 @@ int bwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
                (aligned16(nv) ? kAlV : 0) | (aligned16(no) ? kAlO : 0) |
                (aligned16(ndo) ? kAlDO : 0) | (aligned16(ndq) ? kAlDQ : 0) |
                (aligned16(ndk) ? kAlDK : 0) | (aligned16(ndv) ? kAlDV : 0);
+  if (p->s.bm.bits && !bwd_block_mask_ok(*p, DType(a->dtype)))
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "block_mask backward needs head_dim >= 64 and 16-byte aligned rows with row "
+                "strides >= head_dim for 16-bit inputs");
   return SDPA_OK;
 }
 
@@ -703,6 +736,34 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     p.count_k = sk.count;
   }
   if ((e = launch_bwd(p, DType(a.dtype), st)) != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+int sdpa_block_mask_build(const sdpa_block_mask_t* mask, int32_t seqlen_q, int32_t seqlen_k,
+                          void* stream) {
+  if (!mask) return fail(SDPA_ERR_NULL, "mask is NULL");
+  if (!mask->bits || !mask->kv_count || !mask->kv_list || !mask->q_count || !mask->q_list)
+    return fail(SDPA_ERR_NULL, "block_mask has a NULL array");
+  if (mask->batch < 1 || mask->heads < 1 || int64_t(mask->batch) * mask->heads > INT32_MAX)
+    return fail(SDPA_ERR_SHAPE, "block_mask batch=%d heads=%d", mask->batch, mask->heads);
+  if (seqlen_q < 1 || seqlen_k < 1 || seqlen_q > kMaxSeqlen || seqlen_k > kMaxSeqlen)
+    return fail(SDPA_ERR_SHAPE, "seqlen_q=%d seqlen_k=%d", seqlen_q, seqlen_k);
+  BmBuildParams bp;
+  bp.bits = mask->bits;
+  bp.kv_count = mask->kv_count;
+  bp.kv_list = mask->kv_list;
+  bp.q_count = mask->q_count;
+  bp.q_list = mask->q_list;
+  bp.planes = int64_t(mask->batch) * mask->heads;
+  bp.sq = seqlen_q;
+  bp.sk = seqlen_k;
+  bp.nqb = (seqlen_q + kMaskBlock - 1) / kMaskBlock;
+  bp.nkb = (seqlen_k + kMaskBlock - 1) / kMaskBlock;
+  bp.words = (seqlen_k + 63) / 64;
+  if (bp.planes * bp.nqb > INT32_MAX || bp.planes * bp.nkb > INT32_MAX)
+    return fail(SDPA_ERR_SHAPE, "block_mask too large for one launch");
+  hipError_t e = launch_block_mask_build(bp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block mask build launch");
   return ok();
 }
 

@@ -512,7 +512,7 @@ struct Tile32 {
   }
 };
 
-template <int D>
+template <int D, bool BSM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
   constexpr int BM = kBwdQ32, BN = 32, H2 = D / 2, NDB = D / 32;
   using T = Tile32<D>;
@@ -563,8 +563,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
+  // block-sparse mask: the 128-key blocks of this 128-row block row replace [kt0, kt1)
+  constexpr int TPB = kMaskBlock / BN;
+  int64_t plane = 0, lrow = 0;
+  int nt = kt1 - kt0;
+  if constexpr (BSM) {
+    static_assert(BM == kMaskBlock, "block rows");
+    plane = bm_plane(s.bm, w.b, w.h);
+    lrow = plane * s.bm.nqb + q0 / kMaskBlock;
+    nt = min(max(s.bm.kv_count[lrow], 0), s.bm.nkb) * TPB;
+  }
   T ktile, vtile;
-  for (int t = kt0; t < kt1; ++t) {
+  for (int it = 0; it < nt; ++it) {
+    int t = kt0 + it;
+    bool part = false;
+    if constexpr (BSM) {
+      const int e = s.bm.kv_list[lrow * s.bm.nkb + it / TPB];
+      t = min(max(e >> 1, 0), s.bm.nkb - 1) * TPB + it % TPB;
+      part = (e & 1) != 0;
+    }
     const int kbase = t * BN;
     ktile.load(kb, p.k.ss, kbase, g.sk, p.aligned & kAlK);
     vtile.load(vb, p.v.ss, kbase, g.sk, p.aligned & kAlV);
@@ -573,7 +590,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
     vtile.store(sv_);
     __syncthreads();
     if (kbase < wj1 && kbase + BN > wj0) {
-      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
+      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN) && !part;
+      // element bits of this row's 32 keys (a 32-key tile is dword t of the row)
+      const uint32_t mb = part ? bm_dword(s.bm, plane, s.sq, s.sk, qi, t) : ~0u;
       f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
       for (int u = 0; u < H2 / 4; ++u) {
@@ -588,7 +607,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pr = fast_exp2(st[r] * s.scale_log2 - lse2);
-        if (!full && !visible(s, g, qi, kbase + 8 * (r >> 2) + 4 * hf + (r & 3))) pr = 0.f;
+        if (!full && !(visible(s, g, qi, kbase + 8 * (r >> 2) + 4 * hf + (r & 3)) &&
+                       ((mb >> (8 * (r >> 2) + 4 * hf + (r & 3))) & 1u)))
+          pr = 0.f;
         ds[r] = pr * (dp[r] - dl);
       }
 #pragma unroll
@@ -612,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq32_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool BSM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
   constexpr int BK = kBwdK32, BQ = 32, H2 = D / 2, NDB = D / 32;
   using T = Tile32<D>;
@@ -666,7 +687,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
     const int h = hk * s.group + gi;
     const float* qb = static_cast<const float*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss;
     const float* gb = static_cast<const float*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh + g.qrow0 * p.dout.ss;
-    for (int t = qt0; t < qt1; ++t) {
+    // block-sparse mask: the 128-row blocks of this 128-key block column replace [qt0, qt1)
+    constexpr int TPQ = kMaskBlock / BQ;
+    int64_t plane = 0, lcol = 0;
+    int nt = qt1 - qt0;
+    if constexpr (BSM) {
+      static_assert(BK == kMaskBlock, "block columns");
+      plane = bm_plane(s.bm, w.b, h);
+      lcol = plane * s.bm.nkb + k0 / kMaskBlock;
+      nt = min(max(s.bm.q_count[lcol], 0), s.bm.nqb) * TPQ;
+    }
+    for (int it = 0; it < nt; ++it) {
+      int t = qt0 + it;
+      bool part = false;
+      if constexpr (BSM) {
+        const int e = s.bm.q_list[lcol * s.bm.nqb + it / TPQ];
+        t = min(max(e >> 1, 0), s.bm.nqb - 1) * TPQ + it % TPQ;
+        part = (e & 1) != 0;
+      }
       const int qbase = t * BQ;
       qtile.load(qb, p.q.ss, qbase, g.sq, p.aligned & kAlQ);
       gtile.load(gb, p.dout.ss, qbase, g.sq, p.aligned & kAlDO);
@@ -688,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
       }
       __syncthreads();
       if (qbase < wi1 && qbase + BQ > wi0) {
-        const bool full = tile_full(s, g, qbase, min(qbase + BQ, g.sq), kw0, kw1);
+        const bool full = tile_full(s, g, qbase, min(qbase + BQ, g.sq), kw0, kw1) && !part;
         f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
         for (int u = 0; u < H2 / 4; ++u) {
@@ -704,7 +742,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv32_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const int ql = 8 * (r >> 2) + 4 * hf + (r & 3);
           float x = fast_exp2(st[r] * s.scale_log2 - slse_[ql]);
-          if (!full && !visible(s, g, qbase + ql, kj)) x = 0.f;
+          // element bit of (query row, this lane's key): bit l32 of dword kw0 / 32 of the row
+          if (!full && !(visible(s, g, qbase + ql, kj) &&
+                         (!part || ((bm_dword(s.bm, plane, s.sq, s.sk, qbase + ql, kw0 / 32) >> l32) & 1u))))
+            x = 0.f;
           pr[r] = x;
           ds[r] = x * (dp[r] - sdl_[ql]);
         }
@@ -779,7 +820,7 @@ struct DqP {
   static constexpr int LDS = (NSK + NSV) * TB;
 };
 
-template <bool BF, int D, int W>
+template <bool BF, int D, int W, bool BSM>
 __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds, int bid) {
   constexpr int BM = 32 * W, BN = DqP<D, W>::BN, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DqP<D, W>::TB, NDMA = BN * CPR / NT;
@@ -818,6 +859,33 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
     wf0 = int(clamp64(a, 0, int64_t(1) << 30));
     wf1 = int(clamp64(b, wf0, int64_t(1) << 30));
   }
+
+  // Block-sparse mask: the 128-key block list of this 128-row block row, staged in LDS,
+  // replaces the tile range [kt0, kt1); past the last step a tile beyond every key.
+  constexpr int TPB = kMaskBlock / BN;
+  __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  int nbm = 0;
+  int64_t plane = 0;
+  if constexpr (BSM) {
+    plane = bm_plane(s.bm, w.b, w.h);
+    const int64_t row = plane * s.bm.nqb + q0 / kMaskBlock;
+    nbm = min(max(s.bm.kv_count[row], 0), s.bm.nkb);
+    for (int i = tid; i < nbm; i += NT) bm_list[i] = s.bm.kv_list[row * s.bm.nkb + i];
+    __syncthreads();
+  }
+  auto tile_at = [&](int i) -> int {
+    if constexpr (BSM) {
+      if (i >= nbm * TPB) return s.bm.nkb * TPB;
+      const int e = __builtin_amdgcn_readfirstlane(bm_list[i / TPB]);
+      return min(max(e >> 1, 0), s.bm.nkb - 1) * TPB + i % TPB;
+    } else {
+      return kt0 + i;
+    }
+  };
+  auto partial_at = [&](int i) -> bool {
+    if constexpr (BSM) return (__builtin_amdgcn_readfirstlane(bm_list[i / TPB]) & 1) != 0;
+    return false;
+  };
 
   // Scores enter exp2 as fma(s, c, -LSE log2e) with c = |scale| log2e; a negative scale
   // is applied by negating q (exact).  dQ takes the signed scale at the end.
@@ -892,21 +960,24 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
     }
   };
   // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
-  auto grad = [&](int t, const f32x16_t& st, const f32x16_t& dp, uint4(&dsf)[NPC]) {
+  auto grad = [&](int t, bool part, const f32x16_t& st, const f32x16_t& dp, uint4(&dsf)[NPC]) {
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pr = fast_exp2(__builtin_fmaf(st[r], c, -lse2));
       ds[r] = pr * (dp[r] - dl);
     }
-    if (t < wf0 || t >= wf1) {
+    if (part || t < wf0 || t >= wf1) {
       asm volatile("" ::: "memory");
       const int base_rel = t * BN - qi - g.off + 4 * hf;
       const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+      // element bits of this row's 32 keys (a 32-key tile is dword t of the row)
+      const uint32_t mb = part ? bm_dword(s.bm, plane, s.sq, s.sk, qi, t) : ~0u;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rel = base_rel + 8 * (r >> 2) + (r & 3);
-        ds[r] = (rel >= s.lo_rel && rel <= hi_eff) ? ds[r] : 0.f;
+        const bool bit = (mb >> (8 * (r >> 2) + 4 * hf + (r & 3))) & 1u;
+        ds[r] = (rel >= s.lo_rel && rel <= hi_eff && bit) ? ds[r] : 0.f;
       }
     }
 #pragma unroll
@@ -925,12 +996,12 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
       }
   };
 
-  const int n = kt1 - kt0;
+  const int n = BSM ? nbm * TPB : kt1 - kt0;
   if (n > 0) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      issue_k(kt0 + j, j);
-      issue_v(kt0 + j, j);
+      issue_k(tile_at(j), j);
+      issue_v(tile_at(j), j);
     }
     vm_wait<2 * NDMA>();
     lds_barrier();
@@ -941,12 +1012,12 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   f32x16_t sa, da, sb, db_;
   if (n > 0) products(0, 0, sa, da);
   for (int i = 0; i < n; ++i) {
-    const int ph = i & 3, t = kt0 + i;
-    issue_k(t + 3, (ph + 3) & 3);
-    issue_v(t + 3, (ph + 3) & 3);
+    const int ph = i & 3;
+    issue_k(tile_at(i + 3), (ph + 3) & 3);
+    issue_v(tile_at(i + 3), (ph + 3) & 3);
     products((ph + 1) & 3, (ph + 1) & 3, sb, db_);  // past the last tile: unused
     uint4 dsf[NPC];
-    grad(t, sa, da, dsf);
+    grad(tile_at(i), partial_at(i), sa, da, dsf);
     dq_update(ph, dsf);
     vm_wait<2 * NDMA>();
     lds_barrier();
@@ -983,7 +1054,7 @@ struct DkdvP {
   static constexpr int LDS = NS * SB;
 };
 
-template <bool BF, int D, int W>
+template <bool BF, int D, int W, bool BSM>
 __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid) {
   constexpr int BK = 32 * W, BQ = DkdvP<D, W>::BQ, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DkdvP<D, W>::TB, NDMA = BQ * CPR / NT;
@@ -1010,7 +1081,57 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   int i0, i1;
   query_range(s, g, k0, kend, i0, i1);
   const int qt0 = i0 / BQ, qt1 = i1 > i0 ? (i1 + BQ - 1) / BQ : qt0;
-  const int nq = qt1 - qt0, n = s.group * nq;
+  const int nq = qt1 - qt0;
+  // Block-sparse mask: this key block's column lists of 128-row blocks, staged in LDS.  A
+  // mask shared by all q heads has one list (item it: head it / nper, list position
+  // (it % nper) / TPQ); per-head masks are staged head after head with the head's index in
+  // bits 16.. of each entry (entries are below 2 * nqb <= 1024, and the host bounds
+  // group * nqb by the LDS list length).
+  constexpr int TPQ = kMaskBlock / BQ;
+  __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  int n = s.group * nq, nper = 0;
+  if constexpr (BSM) {
+    const int kblk = k0 / kMaskBlock;
+    if (s.bm.nh == 1) {
+      const int64_t col = bm_plane(s.bm, w.b, 0) * s.bm.nkb + kblk;
+      const int cnt = min(min(max(s.bm.q_count[col], 0), s.bm.nqb), kMaskMaxList);
+      for (int i = tid; i < cnt; i += NT) bm_list[i] = s.bm.q_list[col * s.bm.nqb + i];
+      nper = cnt * TPQ;
+      n = s.group * nper;
+    } else {
+      int tot = 0;
+      for (int gi = 0; gi < s.group; ++gi) {
+        const int64_t col = bm_plane(s.bm, w.b, hk * s.group + gi) * s.bm.nkb + kblk;
+        const int cnt = min(min(max(s.bm.q_count[col], 0), s.bm.nqb), kMaskMaxList - tot);
+        for (int i = tid; i < cnt; i += NT) bm_list[tot + i] = (gi << 16) | (s.bm.q_list[col * s.bm.nqb + i] & 0xffff);
+        tot += cnt;
+      }
+      n = tot * TPQ;
+    }
+    __syncthreads();
+  }
+  // item it -> q head (within the group), q tile, and whether its block needs the bits
+  auto item = [&](int it, int& gi, int& qt, bool& part) {
+    if constexpr (BSM) {
+      int e, r;
+      if (s.bm.nh == 1) {
+        gi = it / nper;
+        r = it - gi * nper;
+        e = __builtin_amdgcn_readfirstlane(bm_list[r / TPQ]);
+      } else {
+        const int v = __builtin_amdgcn_readfirstlane(bm_list[it / TPQ]);
+        gi = v >> 16;
+        e = v & 0xffff;
+        r = it;
+      }
+      qt = min(max(e >> 1, 0), s.bm.nqb - 1) * TPQ + r % TPQ;
+      part = (e & 1) != 0;
+    } else {
+      gi = it / nq;
+      qt = qt0 + it % nq;
+      part = false;
+    }
+  };
   const int kw0 = k0 + wave * 32, kw1 = min(kw0 + 32, g.sk);
   const int kj = kw0 + l32;
   // query tiles [wq0, wq1) in which every (query, key) pair of this wave is visible and
@@ -1053,7 +1174,10 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   const i32x4_t rstat = make_rsrc(wave == 0 ? p.lse2 : p.delta, p.ws_rows * 4);
   auto issue = [&](int it, int slot) {
     it = min(it, n - 1);  // past the last item: reload it (never read), keeps wait counts fixed
-    const int h = hk * s.group + it / nq, qbase = (qt0 + it % nq) * BQ;
+    int gi, qt;
+    bool part;
+    item(it, gi, qt, part);
+    const int h = hk * s.group + gi, qbase = qt * BQ;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * qss;
     const uint16_t* gh = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh +
                          g.qrow0 * gss;
@@ -1101,7 +1225,10 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   // P, dS and the dV, dK updates of item `it` (slot sl), given its S and dP
   auto update = [&](int sl, int it, const f32x16_t& st, const f32x16_t& dp) {
     const lds_t* base = lds + sl * SB;
-    const int qbase = (qt0 + it % nq) * BQ;
+    int gi, qt;
+    bool part;
+    item(it, gi, qt, part);
+    const int qbase = qt * BQ;
     // lane = key; register r holds query 8(r/4) + 4hf + r%4 of the tile
     float pr[16], ds[16];
 #pragma unroll
@@ -1117,14 +1244,16 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
         ds[r] = pr[r] * (dp[r] - da[e]);
       }
     }
-    const int qt = qt0 + it % nq;
-    if (qt < wq0 || qt >= wq1) {
+    if (part || qt < wq0 || qt >= wq1) {
       asm volatile("" ::: "memory");
       const int rel0 = kj - qbase - g.off - 4 * hf;
+      const int64_t plane = bm_plane(s.bm, w.b, hk * s.group + gi);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qrow = 8 * (r >> 2) + (r & 3);
-        const bool vis = rel0 - qrow >= s.lo_rel && rel0 - qrow <= s.hi_rel && qbase + 4 * hf + qrow < g.sq;
+        // element bit of (query row, this lane's key): bit l32 of dword kw0 / 32 of the row
+        const bool bit = !part || ((bm_dword(s.bm, plane, s.sq, s.sk, qbase + 4 * hf + qrow, kw0 / 32) >> l32) & 1u);
+        const bool vis = rel0 - qrow >= s.lo_rel && rel0 - qrow <= s.hi_rel && qbase + 4 * hf + qrow < g.sq && bit;
         pr[r] = vis ? pr[r] : 0.f;
         ds[r] = vis ? ds[r] : 0.f;
       }
@@ -1195,26 +1324,26 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
 template <bool BF, int D, int W>
 __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dq16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DqP<D, W>::LDS];
-  dq16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
+  dq16p_body<BF, D, W, false>(p, (lds_t*)smem_, blockIdx.x);
 }
 
 template <bool BF, int D, int W>
 __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dkdv16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DkdvP<D, W>::LDS];
-  dkdv16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
+  dkdv16p_body<BF, D, W, false>(p, (lds_t*)smem_, blockIdx.x);
 }
 
 // dK/dV and dQ in one launch: blocks [0, nk) take key tiles, the rest query tiles.  The two
 // halves are independent, so on small problems they fill the chip together instead of one
 // after the other.
-template <bool BF, int D, int W>
+template <bool BF, int D, int W, bool BSM>
 __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_fused16p_kernel(BwdParams p, int nk) {
   constexpr int L = DqP<D, W>::LDS > DkdvP<D, W>::LDS ? DqP<D, W>::LDS : DkdvP<D, W>::LDS;
   __shared__ __align__(16) char smem_[L];
   if (int(blockIdx.x) < nk)
-    dkdv16p_body<BF, D, W>(p, (lds_t*)smem_, blockIdx.x);
+    dkdv16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, blockIdx.x);
   else
-    dq16p_body<BF, D, W>(p, (lds_t*)smem_, int(blockIdx.x) - nk);
+    dq16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, int(blockIdx.x) - nk);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1262,16 +1391,21 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
     if (kv && q) {
       if (bk + bq <= 0) return hipSuccess;
       prof_begin(st, "bwd_main");
-      hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2>), dim3(unsigned(bk + bq)), dim3(128), 0, st, p, int(bk));
+      if (p.s.bm.bits)
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, true>), dim3(unsigned(bk + bq)), dim3(128), 0, st, p, int(bk));
+      else
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, false>), dim3(unsigned(bk + bq)), dim3(128), 0, st, p, int(bk));
       prof_end(st);
       return hipGetLastError();
     }
+    if (p.s.bm.bits) return hipErrorInvalidValue;  // rejected by validation
     hipError_t e = kv ? go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128)
                       : go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
     if (e != hipSuccess) return e;
     return q ? go(bwd_dq16p_kernel<BF, D, 2>, "bwd_dq", bq, st, p, 128)
              : go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
   } else {
+    if (p.s.bm.bits) return hipErrorInvalidValue;  // rejected by validation
     hipError_t e = go(bwd_dkdv16_kernel<BF, D>, "bwd_dkdv", bk, st, p);
     if (e != hipSuccess) return e;
     return go(bwd_dq16_kernel<BF, D>, "bwd_dq", bq, st, p);
@@ -1280,9 +1414,27 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
 
 template <int D>
 static hipError_t main32(const BwdParams& p, hipStream_t st, int64_t bq, int64_t bk) {
-  hipError_t e = go(bwd_dkdv32_kernel<D>, "bwd_dkdv", bk, st, p);
+  if (p.s.bm.bits) {
+    hipError_t e = go(bwd_dkdv32_kernel<D, true>, "bwd_dkdv", bk, st, p);
+    if (e != hipSuccess) return e;
+    return go(bwd_dq32_kernel<D, true>, "bwd_dq", bq, st, p);
+  }
+  hipError_t e = go(bwd_dkdv32_kernel<D, false>, "bwd_dkdv", bk, st, p);
   if (e != hipSuccess) return e;
-  return go(bwd_dq32_kernel<D>, "bwd_dq", bq, st, p);
+  return go(bwd_dq32_kernel<D, false>, "bwd_dq", bq, st, p);
+}
+
+bool bwd_block_mask_ok(const BwdParams& p, DType dt) {
+  if (dt == DType::F32) return true;
+  if (p.s.d < 64) return false;
+  constexpr int32_t need_kv = kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV;
+  constexpr int32_t need_q = kAlQ | kAlK | kAlV | kAlDO | kAlDQ;
+  const bool kv = p.s.d == 64 ? pipelined_ok<64>(p, p.s.sq, p.q.ss, p.dout.ss, need_kv)
+                              : pipelined_ok<128>(p, p.s.sq, p.q.ss, p.dout.ss, need_kv);
+  const bool q = p.s.d == 64 ? pipelined_ok<64>(p, p.s.sk, p.k.ss, p.v.ss, need_q)
+                             : pipelined_ok<128>(p, p.s.sk, p.k.ss, p.v.ss, need_q);
+  // per-head masks stage every head's column list of a key block in LDS
+  return kv && q && (p.s.bm.nh == 1 || int64_t(p.s.group) * p.s.bm.nqb <= kMaskMaxList);
 }
 
 hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {

@@ -49,6 +49,8 @@ int plan(const sdpa_desc_t* d, int cp, const int32_t* hop_order, Plan& p) {
   if (d->layout == SDPA_LAYOUT_THD)
     return sdpa::set_error(SDPA_ERR_UNSUPPORTED, "context-parallel emulation supports BSHD, SBHD and BHSD");
   if (d->layout < 0 || d->layout > SDPA_LAYOUT_BHSD) return sdpa::set_error(SDPA_ERR_ARG, "bad layout");
+  if (d->block_mask)
+    return sdpa::set_error(SDPA_ERR_UNSUPPORTED, "context-parallel emulation takes no block_mask");
   if (d->seqlen_q != d->seqlen_k)
     return sdpa::set_error(SDPA_ERR_SHAPE, "context-parallel emulation needs seqlen_q == seqlen_k");
   if (d->seqlen_q <= 0 || d->seqlen_q % (2 * cp) != 0)

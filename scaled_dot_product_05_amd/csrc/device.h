@@ -235,6 +235,19 @@ __host__ __device__ __forceinline__ int tpos(int r) {
 }
 
 // One sequence of the batch: first packed row (THD) and its lengths.
+// Block-sparse mask plane of (batch b, q head h): a mask of extent 1 is shared.
+__device__ __forceinline__ int64_t bm_plane(const BlockMaskP& m, int b, int h) {
+  return int64_t(m.nb == 1 ? 0 : b) * m.nh + (m.nh == 1 ? 0 : h);
+}
+
+// Mask bits of query row i for keys 32 dw .. 32 dw + 31 (bit k: key 32 dw + k); 0 for a row
+// or keys outside the (sq, sk) plane.
+__device__ __forceinline__ uint32_t bm_dword(const BlockMaskP& m, int64_t plane, int sq, int sk, int i,
+                                             int dw) {
+  if (i < 0 || i >= sq || dw < 0 || 32 * dw >= sk) return 0u;
+  return reinterpret_cast<const uint32_t*>(m.bits + (plane * sq + i) * int64_t(m.words))[dw];
+}
+
 struct Seq {
   int64_t qrow0, krow0;
   int32_t sq, sk, off;

@@ -346,7 +346,7 @@ __device__ __forceinline__ int swv(int r) {
 
 // QB = query blocks of 32 per wave: with QB = 2 every K or V operand read from LDS feeds two
 // products, halving LDS reads per flop, and each K/V tile serves 256 query rows.
-template <bool BF, int D, int MINB, int QB, int BN>
+template <bool BF, int D, int MINB, int QB, int BN, bool BSM>
 __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   constexpr int BM = 32 * QB * kWaves;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -385,6 +385,35 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   key_range(s, g, q0, qend, j0, j1);
   const int kt0 = j0 / BN;
   const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  // Block-sparse mask: the workgroup's query rows are one 128-row block row; its list of
+  // 128-key blocks (each TPB tiles) is staged in LDS and replaces the range [kt0, kt1).
+  constexpr int TPB = kMaskBlock / BN;
+  __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  int nbm = 0;
+  int64_t plane = 0;
+  if constexpr (BSM) {
+    static_assert(BM == kMaskBlock && kMaskBlock % BN == 0, "block rows");
+    plane = bm_plane(s.bm, w.b, w.h);
+    const int64_t row = plane * s.bm.nqb + q0 / kMaskBlock;
+    nbm = min(max(s.bm.kv_count[row], 0), s.bm.nkb);
+    for (int i = tid; i < nbm; i += kThreads) bm_list[i] = s.bm.kv_list[row * s.bm.nkb + i];
+    __syncthreads();
+  }
+  // tile of step i and whether its block needs the element bits; past the last step a tile
+  // beyond every key (its loads fill with zeros)
+  auto tile_at = [&](int i) -> int {
+    if constexpr (BSM) {
+      if (i >= nbm * TPB) return s.bm.nkb * TPB;
+      const int e = __builtin_amdgcn_readfirstlane(bm_list[i / TPB]);
+      return min(max(e >> 1, 0), s.bm.nkb - 1) * TPB + i % TPB;
+    } else {
+      return kt0 + i;
+    }
+  };
+  auto partial_at = [&](int i) -> bool {
+    if constexpr (BSM) return (__builtin_amdgcn_readfirstlane(bm_list[i / TPB]) & 1) != 0;
+    return false;
+  };
   const int qw0 = q0 + wave * 32 * QB;
   const int qw1 = min(qw0 + 32 * QB, g.sq);
   // key tiles [wf0, wf1) that every row of this wave sees in full (no mask needed); a wave
@@ -492,9 +521,10 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
       }
   };
   // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
-  auto mask = [&](int t, f32x16_t(&st)[QB][NKB]) {
+  // (and, in a partial block of a block-sparse mask, the element bit of (query, key))
+  auto mask = [&](int t, bool part, f32x16_t(&st)[QB][NKB]) {
     const int kbase = t * BN;
-    if (t < wf0 || t >= wf1) {
+    if (part || t < wf0 || t >= wf1) {
       // keeps the compiler from evaluating the mask on every tile as selects
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -502,12 +532,22 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
         const int qi = qw0 + 32 * j + l32;
         const int base_rel = kbase - qi - g.off + 4 * hf;
         const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+        uint32_t mb[NKB];
+#pragma unroll
+        for (int k2 = 0; k2 < NKB; ++k2) mb[k2] = ~0u;
+        if constexpr (BSM) {
+          if (part) {
+#pragma unroll
+            for (int k2 = 0; k2 < NKB; ++k2) mb[k2] = bm_dword(s.bm, plane, s.sq, s.sk, qi, kbase / 32 + k2);
+          }
+        }
 #pragma unroll
         for (int k2 = 0; k2 < NKB; ++k2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
-            st[j][k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[j][k2][r] : kNegInf;
+            const bool bit = (mb[k2] >> (8 * (r >> 2) + 4 * hf + (r & 3))) & 1u;
+            st[j][k2][r] = (rel >= s.lo_rel && rel <= hi_eff && bit) ? st[j][k2][r] : kNegInf;
           }
       }
     }
@@ -580,13 +620,13 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   // barrier waits only for the loads issued one step earlier (NS = 3) or for all (NS = 2).
   // Loads are issued whether or not the tile exists: past the sequence end the buffer
   // range is empty and the slot fills with zeros, which keeps the wait counts fixed.
-  const int n = kt1 - kt0;
+  const int n = BSM ? nbm * TPB : kt1 - kt0;
   f32x16_t sa[QB][NKB], sb[QB][NKB];
   if (n > 0) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      issue_k(kt0 + j, j);
-      if (j + 1 < NS) issue_v(kt0 + j, j);
+      issue_k(tile_at(j), j);
+      if (j + 1 < NS) issue_v(tile_at(j), j);
     }
     vm_wait<2 * (NS - 2) * NDMA>();
     lds_barrier();
@@ -599,10 +639,9 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   // step has no branch between the two cases.
   auto step = [&](auto I, int i, f32x16_t(&cur)[QB][NKB], f32x16_t(&nxt)[QB][NKB]) {
     constexpr int ph = decltype(I)::value % NS;
-    const int t = kt0 + i;
-    issue_k(t + NS, ph);
-    issue_v(t + NS - 1, (ph + NS - 1) % NS);
-    mask(t, cur);
+    issue_k(tile_at(i + NS), ph);
+    issue_v(tile_at(i + NS - 1), (ph + NS - 1) % NS);
+    mask(tile_at(i), partial_at(i), cur);
     uint4 pf[QB][NPC];
     scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
     softmax(cur, pf);
@@ -666,7 +705,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
 // for the fp64 form and row 4*(l/16) + r for the fp32 form.  Each wave owns 32 queries
 // (two 16-column blocks); a K/V tile is 32 keys (two 16-row blocks).
 // ----------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool BSM>
 __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdParams p) {
   constexpr int BM = kFwdBM, BN = kFwdBN32;
   constexpr int KP = D + 4;  // row pitch in floats
@@ -702,6 +741,28 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdPa
   const int qw1 = min(qw0 + 32, g.sq);
   int wj0 = 0, wj1 = 0;
   if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+  // block-sparse mask: the list of 128-key blocks of this 128-row block row, in LDS
+  constexpr int TPB = kMaskBlock / BN;
+  __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  int nbm = 0;
+  int64_t plane = 0;
+  if constexpr (BSM) {
+    static_assert(BM == kMaskBlock, "block rows");
+    plane = bm_plane(s.bm, w.b, w.h);
+    const int64_t row = plane * s.bm.nqb + q0 / kMaskBlock;
+    nbm = min(max(s.bm.kv_count[row], 0), s.bm.nkb);
+    for (int i = tid; i < nbm; i += kThreads) bm_list[i] = s.bm.kv_list[row * s.bm.nkb + i];
+    __syncthreads();
+  }
+  const int nt = BSM ? nbm * TPB : kt1 - kt0;
+  auto tile_at = [&](int i) -> int {
+    if constexpr (BSM) {
+      const int e = __builtin_amdgcn_readfirstlane(bm_list[i / TPB]);
+      return min(max(e >> 1, 0), s.bm.nkb - 1) * TPB + i % TPB;
+    } else {
+      return kt0 + i;
+    }
+  };
   const double scale = double(s.scale);
   const double log2e = 1.4426950408889634;
 
@@ -747,17 +808,20 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdPa
     }
   };
 
-  if (kt0 < kt1) {
-    gload(kt0);
+  if (nt > 0) {
+    gload(tile_at(0));
     sstore(0);
   }
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) gload(kt + 1);
+  for (int it = 0; it < nt; ++it) {
+    const int kt = tile_at(it);
+    const int buf = it & 1;
+    const bool more = it + 1 < nt;
+    if (more) gload(tile_at(it + 1));
     const int kbase = kt * BN;
+    bool part = false;
+    if constexpr (BSM) part = (__builtin_amdgcn_readfirstlane(bm_list[it / TPB]) & 1) != 0;
     if (kbase < wj1 && kbase + BN > wj0) {
       // S^T blocks (key block kb, query block qb) in fp64
       f64x4_t st[2][2];
@@ -779,17 +843,21 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void fwd32_kernel(FwdPa
           }
         }
       }
-      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN);
+      const bool full = tile_full(s, g, qw0, qw1, kbase, kbase + BN) && !part;
 #pragma unroll
       for (int qb2 = 0; qb2 < 2; ++qb2) {
         const int qi = qw0 + 16 * qb2 + l16;
+        // element bits of this row's 32 keys (tile kt is dword kt of the row)
+        const uint32_t mb = part ? bm_dword(s.bm, plane, s.sq, s.sk, qi, kt) : ~0u;
         double mx = -__builtin_inf();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             double t = st[k2][qb2][r] * scale;
-            if (!full && !visible(s, g, qi, kbase + 16 * k2 + 4 * r + sg)) t = -__builtin_inf();
+            if (!full && !(visible(s, g, qi, kbase + 16 * k2 + 4 * r + sg) &&
+                           ((mb >> (16 * k2 + 4 * r + sg)) & 1u)))
+              t = -__builtin_inf();
             st[k2][qb2][r] = t;
             mx = fmax(mx, t);
           }
@@ -866,6 +934,18 @@ static hipError_t go(K kernel, int blocks, hipStream_t st, const FwdParams& p) {
   return hipGetLastError();
 }
 
+// The pipelined kernel addresses K/V rows with 32-bit buffer offsets (a tile spans kFwdBNP
+// rows) and relies on rows of at least D elements, so that every row past the sequence end
+// lies wholly outside the buffer range.
+static bool fwd_pipelined(const FwdParams& p) {
+  constexpr int need = kAlQ | kAlK | kAlV | kAlO;
+  const int64_t kv_ss = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
+  return (p.aligned & need) == need && p.k.ss >= p.s.d && p.v.ss >= p.s.d &&
+         (int64_t(p.s.sk) + 4 * kFwdBNP) * kv_ss * 2 < (int64_t(1) << 31);
+}
+
+bool fwd_block_mask_ok(const FwdParams& p, DType dt) { return dt == DType::F32 || fwd_pipelined(p); }
+
 template <bool BF, int D, int BN, int MINB>
 static hipError_t go16(const FwdParams& p, hipStream_t st) {
   constexpr int BM = 32 * kWaves;
@@ -879,17 +959,15 @@ static hipError_t go16(const FwdParams& p, hipStream_t st) {
     // 64 query rows per wave when the grid still fills the chip twice over
     const int64_t wide = fwd_grid(p, 2 * BM);
     if (al0 && p.k.ss >= D && p.v.ss >= D && (int64_t(p.s.sk) + 4 * 32) * kv_ss0 * 2 < (int64_t(1) << 31) &&
-        !p.s.thd && wide >= kFwdWideMinBlocks)
-      return go(fwd16p_kernel<BF, D, MINB, 2, 32>, int(wide), st, p);
+        !p.s.thd && !p.s.bm.bits && wide >= kFwdWideMinBlocks)
+      return go(fwd16p_kernel<BF, D, MINB, 2, 32, false>, int(wide), st, p);
   }
   const bool al = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
-  // The pipelined kernel addresses K/V rows with 32-bit buffer offsets (a tile spans
-  // kFwdBNP rows) and relies on rows of at least D elements, so that every row past the
-  // sequence end lies wholly outside the buffer range.
-  const int64_t kv_ss = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
-  const bool pipe = al && p.k.ss >= D && p.v.ss >= D &&
-                    (int64_t(p.s.sk) + 4 * kFwdBNP) * kv_ss * 2 < (int64_t(1) << 31);
-  if (pipe) return go(fwd16p_kernel<BF, D, MINB, 1, kFwdBNP>, int(blocks), st, p);
+  if (fwd_pipelined(p)) {
+    if (p.s.bm.bits) return go(fwd16p_kernel<BF, D, MINB, 1, kFwdBNP, true>, int(blocks), st, p);
+    return go(fwd16p_kernel<BF, D, MINB, 1, kFwdBNP, false>, int(blocks), st, p);
+  }
+  if (p.s.bm.bits) return hipErrorInvalidValue;  // rejected by validation
   return al ? go(fwd16_kernel<BF, D, BN, MINB, true>, int(blocks), st, p)
             : go(fwd16_kernel<BF, D, BN, MINB, false>, int(blocks), st, p);
 }
@@ -910,9 +988,14 @@ hipError_t launch_fwd(const FwdParams& p, DType dt, hipStream_t st) {
   const int64_t blocks = fwd_grid(p, kFwdBM);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (s.d == 32) return go(fwd32_kernel<32>, int(blocks), st, p);
-  if (s.d == 64) return go(fwd32_kernel<64>, int(blocks), st, p);
-  return go(fwd32_kernel<128>, int(blocks), st, p);
+  if (s.bm.bits) {
+    if (s.d == 32) return go(fwd32_kernel<32, true>, int(blocks), st, p);
+    if (s.d == 64) return go(fwd32_kernel<64, true>, int(blocks), st, p);
+    return go(fwd32_kernel<128, true>, int(blocks), st, p);
+  }
+  if (s.d == 32) return go(fwd32_kernel<32, false>, int(blocks), st, p);
+  if (s.d == 64) return go(fwd32_kernel<64, false>, int(blocks), st, p);
+  return go(fwd32_kernel<128, false>, int(blocks), st, p);
 }
 
 }  // namespace sdpa

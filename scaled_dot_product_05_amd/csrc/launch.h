@@ -11,5 +11,9 @@ hipError_t launch_fwd(const FwdParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_merge_fwd(const MergeParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_merge_bwd(const MergeParams& p, DType dtype, hipStream_t stream);
+hipError_t launch_block_mask_build(const BmBuildParams& p, hipStream_t stream);
+// Whether the kernels chosen for these parameters take a block-sparse mask.
+bool fwd_block_mask_ok(const FwdParams& p, DType dtype);
+bool bwd_block_mask_ok(const BwdParams& p, DType dtype);
 
 }  // namespace sdpa

@@ -27,6 +27,20 @@ struct StatView {
 constexpr int32_t kUnbounded = 1 << 30;
 constexpr int32_t kMaxSeqlen = (1 << 28) - 1;
 
+// Block-sparse mask: element bits plus the block table built from them (128 x 128 blocks).
+// bits == nullptr: no block mask.
+constexpr int kMaskBlock = 128;
+constexpr int kMaskMaxList = 512;  // longest block list a workgroup stages in LDS
+struct BlockMaskP {
+  const uint64_t* bits;     // [nb][nh][sq][words]: bit j of word w of row i = key 64w+j
+  const int32_t* kv_count;  // [nb][nh][nqb]
+  const int32_t* kv_list;   // [nb][nh][nqb][nkb]: 2*kb + partial, increasing kb
+  const int32_t* q_count;   // [nb][nh][nkb]
+  const int32_t* q_list;    // [nb][nh][nkb][nqb]: 2*qb + partial, increasing qb
+  int32_t nb, nh;           // 1 = shared over batch / q heads
+  int32_t nqb, nkb, words;
+};
+
 struct Shape {
   int32_t batch, sq, sk, hq, hk, group, d;
   int32_t thd;
@@ -39,6 +53,7 @@ struct Shape {
   int32_t bottom_right;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
+  BlockMaskP bm;
 };
 
 // THD work item: sequence index and tile index within that sequence.
@@ -82,6 +97,17 @@ struct MergeParams {
   View xa, xb, x, g, dxa, dxb;
   StatView la, lb, l, glse, dla, dlb;
   int32_t aligned;       // all x-like row starts 16-byte aligned
+};
+
+// Block-table builder (sdpa_block_mask_build).
+struct BmBuildParams {
+  const uint64_t* bits;
+  int32_t* kv_count;
+  int32_t* kv_list;
+  int32_t* q_count;
+  int32_t* q_list;
+  int64_t planes;
+  int32_t sq, sk, nqb, nkb, words;
 };
 
 // THD scheduler: builds a work list sorted by decreasing cost from device cu_seqlens.

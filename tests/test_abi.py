@@ -26,11 +26,11 @@ def header_functions():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = S.lib()
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.exported_symbols())
-    assert S.sdpa_version() == 2
+    assert S.sdpa_version() == 3
 
 
 def status_of(fn, *args):
@@ -207,3 +207,83 @@ def test_cp_validation_on_host():
     ws = torch.empty(S.sdpa_cp_workspace_size(pr.desc, 2), dtype=torch.uint8)
     with pytest.raises(S.SdpaError):
         S.sdpa_cp_fwd(pr.desc, 2, [0, 0], q, q, q, o, lse, ws)
+
+
+class _FakeMask:
+    """Host stand-in for a device BlockMask: validation never reads the arrays."""
+
+    def __init__(self, batch, heads):
+        self.buf = torch.zeros(64, dtype=torch.int64)
+        p = self.buf.data_ptr()
+        self.desc = S.BlockMaskDesc(batch, heads, p, p, p, p, p)
+
+
+def _bm_problem(dtype, d=64, sq=512, sk=512, hq=4, hk=4, b=2, mask=None, layout="bshd",
+                aligned=True):
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    q = torch.zeros(b, sq, hq, d, dtype=tdt)
+    k = torch.zeros(b, sk, hk, d, dtype=tdt)
+    v = torch.zeros(b, sk, hk, d, dtype=tdt)
+    if not aligned:  # rows that start 2 elements past a 16-byte boundary
+        big = torch.zeros(b, sq, hq, d + 2, dtype=tdt)
+        q = big[..., 2:]
+    o = torch.zeros(b, sq, hq, d, dtype=tdt)
+    lse = torch.zeros(b, hq, sq, dtype=torch.float32)
+    desc = S.make_desc(layout, dtype, b, sq, sk, hq, hk, d, 0.125, (-1, 0), block_mask=mask)
+    return desc, q, k, v, o, lse
+
+
+def test_block_mask_validation_on_host():
+    m = _FakeMask(1, 1)
+    for dt in ("bf16", "f16", "f32"):
+        desc, q, k, v, o, lse = _bm_problem(dt, mask=m)
+        assert fwd_status(desc, q, k, v, o, lse) == "OK"
+        dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+        ws = S.sdpa_bwd_workspace_size(desc)
+        assert status_of(S.sdpa_bwd_validate, desc, q, k, v, o, lse, o.clone(), None, dq, dk, dv,
+                         ws) == "OK"
+    # extents: 1 or the problem's batch / q heads
+    assert fwd_status(*_bm_problem("bf16", mask=_FakeMask(2, 4))) == "OK"
+    assert fwd_status(*_bm_problem("bf16", mask=_FakeMask(3, 1))) == "ERR_SHAPE"
+    assert fwd_status(*_bm_problem("bf16", mask=_FakeMask(1, 2))) == "ERR_SHAPE"
+    # NULL arrays
+    bad = _FakeMask(1, 1)
+    bad.desc.q_list = None
+    assert fwd_status(*_bm_problem("bf16", mask=bad)) == "ERR_NULL"
+    # keys above the staged list length
+    assert fwd_status(*_bm_problem("bf16", sk=512 * 128 + 1, mask=m)) == "ERR_UNSUPPORTED"
+    # 16-bit rows the pipelined kernels cannot take
+    assert fwd_status(*_bm_problem("bf16", mask=m, aligned=False)) == "ERR_UNSUPPORTED"
+    assert fwd_status(*_bm_problem("f32", mask=m, aligned=False)) == "OK"
+    # 16-bit backward at head_dim 32
+    desc, q, k, v, o, lse = _bm_problem("bf16", d=32, mask=m)
+    assert fwd_status(desc, q, k, v, o, lse) == "OK"
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    ws = S.sdpa_bwd_workspace_size(desc)
+    assert status_of(S.sdpa_bwd_validate, desc, q, k, v, o, lse, o.clone(), None, dq, dk, dv,
+                     ws) == "ERR_UNSUPPORTED"
+    # per-head masks: the group's column lists must fit the staged list
+    desc, q, k, v, o, lse = _bm_problem("bf16", sq=128 * 200, sk=256, hq=4, hk=1, b=1,
+                                        mask=_FakeMask(1, 4))
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    ws = S.sdpa_bwd_workspace_size(desc)
+    assert status_of(S.sdpa_bwd_validate, desc, q, k, v, o, lse, o.clone(), None, dq, dk, dv,
+                     ws) == "ERR_UNSUPPORTED"
+    # THD takes no block mask
+    t = torch.zeros(64, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    desc = S.make_desc("thd", "bf16", 1, 64, 64, 2, 2, 64, 0.1, (-1, 0), cu_seqlens_q=cu,
+                       total_q=64, total_k=64, block_mask=m)
+    assert status_of(S.sdpa_fwd_validate, desc, t, t.clone(), t.clone(), t.clone(),
+                     torch.zeros(2, 64), 1 << 20) == "ERR_UNSUPPORTED"
+
+
+def test_block_mask_build_rejects_bad_arguments():
+    m = _FakeMask(1, 1)
+    assert status_of(S.sdpa_block_mask_build, m.desc, 0, 64) == "ERR_SHAPE"
+    assert status_of(S.sdpa_block_mask_build, m.desc, 64, (1 << 28)) == "ERR_SHAPE"
+    bad = _FakeMask(0, 1)
+    assert status_of(S.sdpa_block_mask_build, bad.desc, 64, 64) == "ERR_SHAPE"
+    bad = _FakeMask(1, 1)
+    bad.desc.bits = None
+    assert status_of(S.sdpa_block_mask_build, bad.desc, 64, 64) == "ERR_NULL"

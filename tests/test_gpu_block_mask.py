@@ -1,0 +1,185 @@
+"""GPU parity of the block-sparse mask path (FlexAttention's BlockMask model, PyTorch issue
+135161's create_block_mask / block_mask= calls) against the fp64 oracle.
+
+The block table that sdpa_block_mask_build writes is integer work and must equal the
+oracle's bit for bit.  Attention under a block mask must equal the oracle's plain masked
+attention (element mask AND window) within the forward / gradient tolerances; a mask with
+every bit set must reproduce the unmasked kernels bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_dot_product_05_amd as S
+import synth
+from gpu_util import DEV, check_forward, check_grads, gpu_bhsd, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_mask(mbool):
+    """BlockMask from a boolean [nb, nh, Sq, Sk] mask (bits packed on the host)."""
+    bits = synth.pack_mask(mbool)
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int64)).to(DEV)
+    return S.BlockMask(t, mbool.shape[-2], mbool.shape[-1])
+
+
+def planes(name, nb, nh, sq, sk, **kw):
+    """[nb, nh, Sq, Sk] masks: plane p draws predicate `name` with seed p."""
+    out = np.zeros((nb, nh, sq, sk), bool)
+    for b in range(nb):
+        for h in range(nh):
+            out[b, h] = synth.flex_mask(name, sq, sk, seed=b * nh + h, **kw)
+    return out
+
+
+@pytest.mark.parametrize("name,sq,sk,nb,nh", [
+    ("random_blocks", 640, 520, 2, 3), ("random", 300, 300, 1, 1), ("document", 700, 700, 1, 1),
+    ("causal", 1000, 1000, 1, 1), ("sliding_window_causal", 512, 512, 1, 1),
+    ("prefix", 130, 4000, 1, 2), ("random", 1, 1, 1, 1), ("random_blocks", 129, 65, 2, 1)])
+def test_block_table_matches_oracle(name, sq, sk, nb, nh):
+    say(f"case table {name} Sq={sq} Sk={sk} nb={nb} nh={nh}")
+    m = planes(name, nb, nh, sq, sk, band=200, doc_lengths=[100, 250, 350], density=0.3)
+    bm = gpu_mask(m)
+    torch.cuda.synchronize()
+    kvc, kvl, qc, ql = oracle.block_lists(oracle.block_kinds(m))
+    g_kvc, g_kvl = bm.kv_count.cpu().numpy(), bm.kv_list.cpu().numpy()
+    g_qc, g_ql = bm.q_count.cpu().numpy(), bm.q_list.cpu().numpy()
+    assert (g_kvc == kvc).all() and (g_qc == qc).all()
+    for idx in np.ndindex(*kvc.shape):
+        assert (g_kvl[idx][:kvc[idx]] == kvl[idx][:kvc[idx]]).all(), idx
+    for idx in np.ndindex(*qc.shape):
+        assert (g_ql[idx][:qc[idx]] == ql[idx][:qc[idx]]).all(), idx
+
+
+def run_bm(w, m, backward=True, what=""):
+    """Forward (and backward) under block mask m [nb, nh, Sq, Sk] vs the oracle."""
+    say(f"case {what} {w.dtype} {w.layout} B={w.batch} Sq={w.seqlen_q} Sk={w.seqlen_k} "
+        f"Hq={w.heads_q} Hk={w.heads_kv} D={w.head_dim} win={w.window} al={w.diag_align} "
+        f"mask planes={m.shape[:2]}")
+    q, k, v = to_dev(w)
+    bm = gpu_mask(m)
+    o, lse = S.forward(q, k, v, w.layout, w.scale, w.window, w.diag_align, block_mask=bm)
+    torch.cuda.synchronize()
+    q64, k64, v64 = (synth.f64(synth.to_bhsd(t, w.layout)) for t in (w.q, w.k, w.v))
+    o_ref, lse_ref = oracle.masked_forward(q64, k64, v64, w.scale, m, w.window, w.diag_align)
+    check_forward(gpu_bhsd(o, w), synth.f64(lse), o_ref, lse_ref, w.dtype, "fwd")
+    if not backward:
+        return
+    dq, dk, dv = S.backward(q, k, v, o, lse, w.dout.to(DEV), w.layout, w.scale, w.window,
+                            w.diag_align, block_mask=bm)
+    torch.cuda.synchronize()
+    g64 = synth.f64(synth.to_bhsd(w.dout, w.layout))
+    refs = oracle.masked_backward(q64, k64, v64, g64, w.scale, m, w.window, w.diag_align)
+    check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], refs, w.dtype, "bwd")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("pred", ["sliding_window_causal", "global_causal_v2"])
+def test_issue_135161_predicates(dtype, pred):
+    # the second repro's masks over Q_LEN = KV_LEN = 512 (band 128), 4 heads of 64
+    w = synth.dense(21, 400, dtype, "bshd", 1, 512, 512, 4, 4, 64, 0.125, (-1, -1),
+                    with_grad=True, name="p3")
+    m = synth.flex_mask(pred, 512, 512, band=128)[None, None]
+    run_bm(w, m, what=pred)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_issue_135161_v1_sliced_rows(dtype):
+    # v1: global mask q_idx > kv_idx on query rows sliced from 128 on (Q_LEN 384, KV_LEN 512)
+    w = synth.dense(22, 401, dtype, "bshd", 1, 384, 512, 4, 4, 64, 0.125, (-1, -1),
+                    with_grad=True, name="p3v1")
+    m = synth.flex_mask("global_causal_v1", 384, 512)[None, None]
+    run_bm(w, m, what="global_causal_v1")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f16", 64), ("f32", 32),
+                                     ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("name", ["random_blocks", "document", "random"])
+def test_structured_masks_ragged(dtype, d, name):
+    w = synth.dense(23, 402 + d, dtype, "bshd", 2, 300, 520, 4, 2, d, d ** -0.5, (-1, -1),
+                    with_grad=True, name="bm")
+    m = synth.flex_mask(name, 300, 520, doc_lengths=[90, 150, 280], seed=7, density=0.4)[None, None]
+    run_bm(w, m, what=name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("window,align", [((-1, 0), 0), ((3, 2), 0), ((-1, 0), 1), ((64, 0), 1)])
+def test_mask_and_window(dtype, window, align):
+    w = synth.dense(24, 410, dtype, "bhsd", 1, 333, 400, 4, 4, 64, 0.2, window, align,
+                    with_grad=True, name="bmwin")
+    m = synth.flex_mask("random_blocks", 333, 400, seed=2, density=0.6)[None, None]
+    run_bm(w, m, what=f"random_blocks & window {window}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["bshd", "sbhd"])
+def test_per_batch_and_head_masks_with_groups(dtype, layout):
+    w = synth.dense(25, 420, dtype, layout, 2, 260, 260, 4, 1, 64, 0.125, (-1, -1),
+                    with_grad=True, name="bmplanes")
+    m = planes("random_blocks", 2, 4, 260, 260, density=0.5)
+    run_bm(w, m, what="per-plane random_blocks")
+
+
+def test_empty_rows_and_block_rows():
+    # rows 0..9 and the whole second block row see nothing: O = 0 and LSE = -inf exactly
+    w = synth.dense(26, 430, "bf16", "bshd", 1, 400, 400, 2, 2, 64, 0.125, (-1, -1),
+                    with_grad=True, name="bmempty")
+    m = synth.flex_mask("random", 400, 400, seed=4, density=0.5)
+    m[:10] = False
+    m[128:256] = False
+    run_bm(w, m[None, None], what="empty rows")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_all_ones_mask_reproduces_the_unmasked_kernels_bitwise(dtype, d):
+    w = synth.dense(27, 440, dtype, "bshd", 2, 640, 640, 4, 2, d, d ** -0.5, (-1, 0),
+                    with_grad=True, name="bmones")
+    say(f"case all-ones {dtype} D={d}")
+    q, k, v = to_dev(w)
+    g = w.dout.to(DEV)
+    bm = gpu_mask(np.ones((1, 1, 640, 640), bool))
+    o0, l0 = S.forward(q, k, v, "bshd", w.scale, w.window)
+    o1, l1 = S.forward(q, k, v, "bshd", w.scale, w.window, block_mask=bm)
+    g0 = S.backward(q, k, v, o0, l0, g, "bshd", w.scale, w.window)
+    g1 = S.backward(q, k, v, o0, l0, g, "bshd", w.scale, w.window, block_mask=bm)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+
+
+def test_head_dim_32_16bit_forward_only():
+    w = synth.dense(28, 450, "bf16", "bshd", 1, 200, 200, 2, 2, 32, 0.2, (-1, -1),
+                    with_grad=True, name="bm32")
+    m = synth.flex_mask("random_blocks", 200, 200, seed=1)[None, None]
+    run_bm(w, m, backward=False, what="D32 forward")
+    q, k, v = to_dev(w)
+    bm = gpu_mask(m)
+    o, lse = S.forward(q, k, v, "bshd", w.scale, block_mask=bm)
+    with pytest.raises(S.SdpaError) as e:
+        S.backward(q, k, v, o, lse, w.dout.to(DEV), "bshd", w.scale, block_mask=bm)
+    assert e.value.name == "ERR_UNSUPPORTED"
+
+
+def test_document_mask_long_sequence_sampled_rows():
+    # a packed-document mask at B2 S4096 H8 D64 bf16: sampled query rows against the oracle
+    s, b, h, d = 4096, 2, 8, 64
+    w = synth.dense(29, 460, "bf16", "bshd", b, s, s, h, h, d, 0.125, (-1, -1), name="bmdoc")
+    lens = [700, 1500, 396, 1000, 500]
+    m = synth.flex_mask("document", s, s, doc_lengths=lens)
+    say(f"case document S={s} B={b} H={h}")
+    q, k, v = to_dev(w)
+    bm = gpu_mask(m[None, None])
+    o, lse = S.forward(q, k, v, "bshd", w.scale, block_mask=bm)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 699, 700, 2199, 2200, 2595, 2596, 3595, 3596, 4095])
+    for bi, hi in ((0, 0), (1, 7)):
+        q64 = synth.f64(w.q[bi, rows, hi])[None, None]
+        k64 = synth.f64(w.k[bi, :, hi])[None, None]
+        v64 = synth.f64(w.v[bi, :, hi])[None, None]
+        o_ref, l_ref = oracle.attention_forward(q64, k64, v64, w.scale, m[rows][None, None])
+        og = synth.f64(o[bi, rows, hi].cpu())
+        lg = synth.f64(lse[bi, hi, rows].cpu())
+        check_forward(og[None, None], lg[None, None], o_ref, l_ref, "bf16", f"rows b={bi} h={hi}")
