@@ -280,6 +280,8 @@ def extra(torch, S, synth, dev):
                               "fwd_TFLOP/s": round(4 * 128 * nvis / (msf * 1e-3) / 1e12, 2),
                               "bwd_TFLOP/s": round(10 * 128 * nvis / (msb * 1e-3) / 1e12, 2)}
 
+    res["block_sparse_bf16"] = block_sparse(torch, S, synth, dev)
+
     # merge kernels, HBM bound: x [4,16,8192,128] fp32, lse [4,16,8192]
     mg = {}
     for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
@@ -317,6 +319,55 @@ def extra(torch, S, synth, dev):
     except Exception:  # pragma: no cover
         pass
     return res
+
+
+def block_sparse(torch, S, synth, dev):
+    """Block-sparse masks (FlexAttention's BlockMask model) at B8 S4096 H8 D64 bf16, forward
+    and backward, next to the native path that computes the same attention: a causal
+    sliding window (band 512) against the window descriptor, and five causal documents per
+    row against THD varlen over the same documents.  FLOPs count the mask's visible pairs."""
+    import numpy as np
+    b, s, h, d = 8, 4096, 8, 64
+    w = synth.target(b=b, s=s, h=h, d=d, with_grad=True)
+    q, k, v, g = (t.to(dev) for t in (w.q, w.k, w.v, w.dout))
+    docs = [700, 1500, 396, 1000, 500]
+    out = {}
+    for name, m, native in (
+            ("sliding_window_causal_512", synth.flex_mask("sliding_window_causal", s, s, band=512),
+             "window"),
+            ("document_5_causal", synth.flex_mask("document", s, s, doc_lengths=docs), "thd")):
+        bits = torch.from_numpy(np.ascontiguousarray(synth.pack_mask(m[None, None])).view(np.int64)).to(dev)
+        ms_build = time_calls(torch, lambda: S.BlockMask(bits, s, s))
+        bm = S.BlockMask(bits, s, s)
+        nvis = b * h * int(m.sum())
+        o, lse = S.forward(q, k, v, "bshd", w.scale, block_mask=bm)
+        msf = time_calls(torch, lambda: S.forward(q, k, v, "bshd", w.scale, block_mask=bm, out=o, lse=lse))
+        msb = time_calls(torch, lambda: S.backward(q, k, v, o, lse, g, "bshd", w.scale, block_mask=bm))
+        if native == "window":
+            nf = lambda: S.forward(q, k, v, "bshd", w.scale, (512, 0), out=o, lse=lse)
+            S.forward(q, k, v, "bshd", w.scale, (512, 0), out=o, lse=lse)
+            nb = lambda: S.backward(q, k, v, o, lse, g, "bshd", w.scale, (512, 0))
+        else:
+            cu = torch.tensor(np.concatenate([[0], np.cumsum(docs * b)]), dtype=torch.int32, device=dev)
+            qt, kt, vt, gt = (t.reshape(b * s, h, d) for t in (q, k, v, g))
+            ot = o.reshape(b * s, h, d)
+            lt = torch.empty(h, b * s, dtype=torch.float32, device=dev)
+            kw = dict(cu_seqlens_q=cu, max_seqlen_q=max(docs))
+            nf = lambda: S.forward(qt, kt, vt, "thd", w.scale, (-1, 0), out=ot, lse=lt, **kw)
+            nf()
+            nb = lambda: S.backward(qt, kt, vt, ot, lt, gt, "thd", w.scale, (-1, 0), **kw)
+        msnf = time_calls(torch, nf)
+        msnb = time_calls(torch, nb)
+        tf = lambda flops, ms: round(flops / (ms * 1e-3) / 1e12, 2)
+        out[name] = {"visible_pairs": nvis, "mask_build_ms": round(ms_build, 4),
+                     "fwd_ms": round(msf, 4), "bwd_ms": round(msb, 4),
+                     "fwd_TFLOP/s": tf(4 * d * nvis, msf), "bwd_TFLOP/s": tf(10 * d * nvis, msb),
+                     f"{native}_fwd_ms": round(msnf, 4), f"{native}_bwd_ms": round(msnb, 4),
+                     f"{native}_fwd_TFLOP/s": tf(4 * d * nvis, msnf),
+                     f"{native}_bwd_TFLOP/s": tf(10 * d * nvis, msnb)}
+        log(f"block mask {name}: build {ms_build:.3f} ms fwd {msf:.3f} ms bwd {msb:.3f} ms; "
+            f"{native} fwd {msnf:.3f} ms bwd {msnb:.3f} ms")
+    return out
 
 
 def cpu_baseline(w, flops_step):

@@ -864,6 +864,9 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   // replaces the tile range [kt0, kt1); past the last step a tile beyond every key.
   constexpr int TPB = kMaskBlock / BN;
   __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  // element bits of partial tiles, loaded with their K tile into the same ring slot: row
+  // 32 w + l of the workgroup, dword t (the tile's 32 keys), one dword per lane of 32
+  __shared__ __align__(16) uint32_t bm_bits[BSM ? 4 * BM : 1];
   int nbm = 0;
   int64_t plane = 0;
   if constexpr (BSM) {
@@ -921,10 +924,23 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
     koff_g[u] = uint32_t(row * kss * 2 + ((pos ^ swb<CPR>(row)) * 16));
     voff_g[u] = uint32_t(row * vss * 2 + ((pos ^ swb<CPR>(row)) * 16));
   }
-  auto issue_k = [&](int t, int slot) {
+  constexpr int NB = BSM ? 1 : 0;  // extra loads per K tile
+  i32x4_t rbits = {0, 0, 0, 0};
+  uint32_t boff = 0;
+  if constexpr (BSM) {
+    rbits = make_rsrc(s.bm.bits + (plane * s.sq + q0) * int64_t(s.bm.words),
+                      int64_t(s.sq - q0) * s.bm.words * 8);
+    boff = uint32_t((wave * 32 + l32) * s.bm.words * 8);
+  }
+  auto issue_k = [&](int t, int slot, bool part) {
     const uint32_t o = uint32_t(t) * kstep;
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) dma16(rk, lds + slot * TB + (u * W + wave) * 1024, koff_g[u] + o);
+    if constexpr (BSM) {
+      // not partial: a load from past the buffer end (fills zeros, reads nothing)
+      if (lane < 32)
+        dma4(rbits, (lds_t*)(bm_bits + slot * BM + wave * 32), part ? boff + uint32_t(t) * 4u : 0x80000000u);
+    }
   };
   auto issue_v = [&](int t, int slot) {
     const uint32_t o = uint32_t(t) * vstep;
@@ -960,7 +976,7 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
     }
   };
   // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
-  auto grad = [&](int t, bool part, const f32x16_t& st, const f32x16_t& dp, uint4(&dsf)[NPC]) {
+  auto grad = [&](int t, bool part, int slot, const f32x16_t& st, const f32x16_t& dp, uint4(&dsf)[NPC]) {
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -972,7 +988,10 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
       const int base_rel = t * BN - qi - g.off + 4 * hf;
       const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
       // element bits of this row's 32 keys (a 32-key tile is dword t of the row)
-      const uint32_t mb = part ? bm_dword(s.bm, plane, s.sq, s.sk, qi, t) : ~0u;
+      uint32_t mb = ~0u;
+      if constexpr (BSM) {
+        if (part) mb = bm_bits[slot * BM + wave * 32 + l32];
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rel = base_rel + 8 * (r >> 2) + (r & 3);
@@ -1000,10 +1019,10 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   if (n > 0) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      issue_k(tile_at(j), j);
+      issue_k(tile_at(j), j, j < n && partial_at(j));
       issue_v(tile_at(j), j);
     }
-    vm_wait<2 * NDMA>();
+    vm_wait<2 * NDMA + NB>();
     lds_barrier();
   }
   // Step i: tile t = kt0 + i in K and V slot t % 4.  The products of tile t+1 are issued
@@ -1013,13 +1032,13 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   if (n > 0) products(0, 0, sa, da);
   for (int i = 0; i < n; ++i) {
     const int ph = i & 3;
-    issue_k(tile_at(i + 3), (ph + 3) & 3);
+    issue_k(tile_at(i + 3), (ph + 3) & 3, i + 3 < n && partial_at(i + 3));
     issue_v(tile_at(i + 3), (ph + 3) & 3);
     products((ph + 1) & 3, (ph + 1) & 3, sb, db_);  // past the last tile: unused
     uint4 dsf[NPC];
-    grad(tile_at(i), partial_at(i), sa, da, dsf);
+    grad(tile_at(i), partial_at(i), ph, sa, da, dsf);
     dq_update(ph, dsf);
-    vm_wait<2 * NDMA>();
+    vm_wait<2 * NDMA + NB>();
     lds_barrier();
     sa = sb;
     da = db_;
@@ -1060,7 +1079,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   constexpr int CPR = D / 8, TB = DkdvP<D, W>::TB, NDMA = BQ * CPR / NT;
   constexpr int NC = D / 16, NDB = D / 32, NPC = BQ / 16;
   constexpr int NS = DkdvP<D, W>::NS, SB = DkdvP<D, W>::SB;
-  constexpr int NL = 2 * NDMA + 1;  // loads per wave per tile
+  constexpr int NL = 2 * NDMA + 1 + (BSM ? 1 : 0);  // loads per wave per tile
   static_assert(W == 2 && NDMA >= 1 && NPC == 2, "tile split");
 
   const Shape& s = p.s;
@@ -1089,6 +1108,9 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   // group * nqb by the LDS list length).
   constexpr int TPQ = kMaskBlock / BQ;
   __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  // element bits of partial items, loaded with the item into the same ring slot: rows
+  // qbase .. qbase + 31, dword kw0 / 32 (the wave's 32 keys), one dword per lane of 32
+  __shared__ __align__(16) uint32_t bm_bits[BSM ? NS * 64 : 1];
   int n = s.group * nq, nper = 0;
   if constexpr (BSM) {
     const int kblk = k0 / kMaskBlock;
@@ -1190,6 +1212,13 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) dma16(rg, dst + TB + (u * W + wave) * 1024, goff[u] + og);
     if (lane < 32) dma4(rstat, dst + 2 * TB + wave * 128, uint32_t(delta_index(s, w.b, h, g, qbase + lane)) * 4u);
+    if constexpr (BSM) {
+      // not partial: a load from past the buffer end (fills zeros, reads nothing)
+      const i32x4_t rb = make_rsrc(s.bm.bits + bm_plane(s.bm, w.b, h) * s.sq * int64_t(s.bm.words),
+                                   int64_t(s.sq) * s.bm.words * 8);
+      const uint32_t o = part ? uint32_t((qbase + l32) * s.bm.words * 8 + (kw0 / 32) * 4) : 0x80000000u;
+      if (lane < 32) dma4(rb, (lds_t*)(bm_bits + slot * 64 + wave * 32), o);
+    }
   };
 
   int ra[NC];
@@ -1247,12 +1276,26 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     if (part || qt < wq0 || qt >= wq1) {
       asm volatile("" ::: "memory");
       const int rel0 = kj - qbase - g.off - 4 * hf;
-      const int64_t plane = bm_plane(s.bm, w.b, hk * s.group + gi);
+      // element bits of (query row, this lane's key): bit l32 of row 8 j + 4 hf + e's dword
+      uint32_t rb[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rb[r] = ~0u;
+      if constexpr (BSM) {
+        if (part) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint4 b4 = *reinterpret_cast<const uint4*>(bm_bits + sl * 64 + wave * 32 + 8 * j + 4 * hf);
+            rb[4 * j] = b4.x;
+            rb[4 * j + 1] = b4.y;
+            rb[4 * j + 2] = b4.z;
+            rb[4 * j + 3] = b4.w;
+          }
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qrow = 8 * (r >> 2) + (r & 3);
-        // element bit of (query row, this lane's key): bit l32 of dword kw0 / 32 of the row
-        const bool bit = !part || ((bm_dword(s.bm, plane, s.sq, s.sk, qbase + 4 * hf + qrow, kw0 / 32) >> l32) & 1u);
+        const bool bit = (rb[r] >> l32) & 1u;
         const bool vis = rel0 - qrow >= s.lo_rel && rel0 - qrow <= s.hi_rel && qbase + 4 * hf + qrow < g.sq && bit;
         pr[r] = vis ? pr[r] : 0.f;
         ds[r] = vis ? ds[r] : 0.f;

@@ -346,8 +346,10 @@ __device__ __forceinline__ int swv(int r) {
 
 // QB = query blocks of 32 per wave: with QB = 2 every K or V operand read from LDS feeds two
 // products, halving LDS reads per flop, and each K/V tile serves 256 query rows.
+// A block-sparse mask asks for one more workgroup per CU at head_dim <= 64 (its lists and
+// bits fit the LDS of three).
 template <bool BF, int D, int MINB, int QB, int BN, bool BSM>
-__global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) void fwd16p_kernel(FwdParams p) {
   constexpr int BM = 32 * QB * kWaves;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TB = BN * D * 2;          // bytes per K or V tile
@@ -389,6 +391,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   // 128-key blocks (each TPB tiles) is staged in LDS and replaces the range [kt0, kt1).
   constexpr int TPB = kMaskBlock / BN;
   __shared__ int32_t bm_list[BSM ? kMaskMaxList : 1];
+  __shared__ __align__(16) uint32_t bm_bits[BSM ? NS * kThreads : 1];
   int nbm = 0;
   int64_t plane = 0;
   if constexpr (BSM) {
@@ -521,10 +524,25 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
       }
   };
   // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
-  // (and, in a partial block of a block-sparse mask, the element bit of (query, key))
-  auto mask = [&](int t, bool part, f32x16_t(&st)[QB][NKB]) {
+  // (and, in a partial block of a block-sparse mask, the element bit of (query, key), as a
+  // pass of its own so that neither pass holds the other's values)
+  auto mask = [&](int t, bool part, int bslot, f32x16_t(&st)[QB][NKB]) {
     const int kbase = t * BN;
-    if (part || t < wf0 || t >= wf1) {
+    if constexpr (BSM) {
+      if (part) {
+        asm volatile("" ::: "memory");
+        static_assert(QB == 1 && NKB == 2, "one 64-key word per row");
+        const int qi = qw0 + l32;
+        const uint2 wb = *reinterpret_cast<const uint2*>(bm_bits + bslot * kThreads + 2 * (qi - q0));
+        const uint32_t mb[2] = {wb.x >> (4 * hf), wb.y >> (4 * hf)};
+#pragma unroll
+        for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st[0][k2][r] = (mb[k2] >> (8 * (r >> 2) + (r & 3))) & 1u ? st[0][k2][r] : kNegInf;
+      }
+    }
+    if (t < wf0 || t >= wf1) {
       // keeps the compiler from evaluating the mask on every tile as selects
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -532,22 +550,12 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
         const int qi = qw0 + 32 * j + l32;
         const int base_rel = kbase - qi - g.off + 4 * hf;
         const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
-        uint32_t mb[NKB];
-#pragma unroll
-        for (int k2 = 0; k2 < NKB; ++k2) mb[k2] = ~0u;
-        if constexpr (BSM) {
-          if (part) {
-#pragma unroll
-            for (int k2 = 0; k2 < NKB; ++k2) mb[k2] = bm_dword(s.bm, plane, s.sq, s.sk, qi, kbase / 32 + k2);
-          }
-        }
 #pragma unroll
         for (int k2 = 0; k2 < NKB; ++k2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
-            const bool bit = (mb[k2] >> (8 * (r >> 2) + 4 * hf + (r & 3))) & 1u;
-            st[j][k2][r] = (rel >= s.lo_rel && rel <= hi_eff && bit) ? st[j][k2][r] : kNegInf;
+            st[j][k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[j][k2][r] : kNegInf;
           }
       }
     }
@@ -621,14 +629,36 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
   // Loads are issued whether or not the tile exists: past the sequence end the buffer
   // range is empty and the slot fills with zeros, which keeps the wait counts fixed.
   const int n = BSM ? nbm * TPB : kt1 - kt0;
+  // Element bits of a partial tile come into LDS with its V tile and in the V tile's ring
+  // slot (both are read at the tile's own step): one dword per thread (row T / 2, dword
+  // T % 2 of the tile's 64-key word).  A tile that is not partial loads from past the
+  // buffer end, which fills zeros and reads nothing.
+  constexpr int NB = BSM ? 1 : 0;  // extra loads per V tile
+  i32x4_t rbits = {0, 0, 0, 0};
+  uint32_t boff = 0;
+  if constexpr (BSM) {
+    rbits = make_rsrc(s.bm.bits + (plane * s.sq + q0) * int64_t(s.bm.words),
+                      int64_t(s.sq - q0) * s.bm.words * 8);
+    boff = uint32_t((tid >> 1) * s.bm.words * 8 + (tid & 1) * 4);
+  }
+  auto issue_bits = [&](int i, int slot) {
+    if constexpr (BSM) {
+      const bool part = i < n && partial_at(i);
+      const uint32_t o = part ? boff + uint32_t(tile_at(i)) * 8u : 0x80000000u;
+      dma4(rbits, (lds_t*)(bm_bits + slot * kThreads + wave * 64), o);
+    }
+  };
   f32x16_t sa[QB][NKB], sb[QB][NKB];
   if (n > 0) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       issue_k(tile_at(j), j);
-      if (j + 1 < NS) issue_v(tile_at(j), j);
+      if (j + 1 < NS) {
+        issue_v(tile_at(j), j);
+        issue_bits(j, j);
+      }
     }
-    vm_wait<2 * (NS - 2) * NDMA>();
+    vm_wait<(NS - 2) * (2 * NDMA + NB)>();
     lds_barrier();
     scores(std::integral_constant<int, 0>(), sa);
     // step 0 reloads K slot 0: every wave must be done reading it first
@@ -641,12 +671,13 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16p_kernel(FwdParams p) {
     constexpr int ph = decltype(I)::value % NS;
     issue_k(tile_at(i + NS), ph);
     issue_v(tile_at(i + NS - 1), (ph + NS - 1) % NS);
-    mask(tile_at(i), partial_at(i), cur);
+    issue_bits(i + NS - 1, (ph + NS - 1) % NS);
+    mask(tile_at(i), partial_at(i), ph, cur);
     uint4 pf[QB][NPC];
     scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
     softmax(cur, pf);
     pv(std::integral_constant<int, ph>(), pf);
-    vm_wait<2 * (NS - 2) * NDMA>();
+    vm_wait<(NS - 2) * (2 * NDMA + NB)>();
     lds_barrier();
   };
   constexpr int U = NS == 2 ? 2 : 6;  // a multiple of NS and of the two score buffers
