@@ -361,6 +361,9 @@ __global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) 
   static_assert(NDMA >= 1 && BN % 32 == 0, "tile split");
   constexpr float kTau = 8.f;
   constexpr int NS = D >= 128 ? kFwdStagesD128 : kFwdStages;  // K and V slots each
+  // direct-to-LDS loads are kept below 128 KiB of LDS (with the block-mask lists and bits):
+  // a backward layout that reached past it lost data it had staged at the bottom of LDS
+  static_assert(2 * NS * TB + 8192 <= 131072, "LDS load destinations below 128 KiB");
   __shared__ __align__(16) char smem_[2 * NS * TB];  // K slots, then V slots
   lds_t* const lds = (lds_t*)smem_;
 
