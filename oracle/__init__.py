@@ -16,12 +16,13 @@ import numpy as np
 from .attention import (NEG_INF, attention_backward, attention_forward, dkdv_cols,
                         dq_rows, forward_rows, merge_backward, merge_forward, window_mask)
 from .block_mask import block_kinds, block_lists
+from .fp8 import e4m3_decode, fp8_forward
 
 __all__ = [
     "NEG_INF", "window_mask", "attention_forward", "attention_backward", "forward_rows",
     "dq_rows", "dkdv_cols", "merge_forward", "merge_backward", "thd_forward",
     "thd_backward", "windowed_forward", "windowed_backward", "block_kinds", "block_lists",
-    "masked_forward", "masked_backward",
+    "masked_forward", "masked_backward", "e4m3_decode", "fp8_forward",
 ]
 
 

@@ -286,3 +286,21 @@ def pack_mask(mask: np.ndarray) -> np.ndarray:
     pad[..., :sk] = mask
     by = np.packbits(pad, axis=-1, bitorder="little")
     return np.ascontiguousarray(by).view("<u8").reshape(mask.shape[:-1] + (words,))
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 (E4M3) inputs: per-tensor delayed-scaling style codes
+# ---------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_codes(x: np.ndarray):
+    """Per-tensor scaled E4M3 codes of fp64 values x, with descale = amax / 448 so that the
+    largest magnitude maps to the largest finite code: returns (uint8 codes as a CPU torch
+    tensor, descale).  The cast is torch's round-to-nearest-even float8_e4m3fn conversion."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = float(np.abs(x).max()) if x.size else 1.0
+    descale = amax / E4M3_MAX if amax > 0 else 1.0
+    scaled = torch.from_numpy(np.ascontiguousarray(x / descale, dtype=np.float32))
+    return scaled.to(torch.float8_e4m3fn).view(torch.uint8), descale

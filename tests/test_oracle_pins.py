@@ -661,3 +661,43 @@ def test_pack_mask_bit_order():
     assert b.shape == (3, 3) and b.dtype == np.uint64
     assert int(b[0, 0]) == 1 and int(b[1, 0]) == 1 << 63 and int(b[1, 1]) == 1
     assert int(b[2, 2]) == 2 and int(b[2, 0]) == 0
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 E4M3 decode (the FP8 forward's oracle is exact attention on decoded inputs)
+# ---------------------------------------------------------------------------------------
+
+def test_e4m3_decode_closed_forms():
+    from oracle import e4m3_decode
+    # 1.0 = 0.0111.000, 448 = 0.1111.110 (largest finite), 2^-9 = 0.0000.001 (smallest
+    # subnormal), 2^-6 = 0.0001.000 (smallest normal), -1.5 = 1.0111.100
+    codes = np.array([0x38, 0x7E, 0x01, 0x08, 0xBC, 0x00, 0x80, 0x07, 0x7F, 0xFF], np.uint8)
+    v = e4m3_decode(codes)
+    assert list(v[:8]) == [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, -1.5, 0.0, -0.0, 7 * 2.0 ** -9]
+    assert np.isnan(v[8]) and np.isnan(v[9])
+
+
+def test_e4m3_decode_equals_torch_float8():
+    from oracle import e4m3_decode
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = e4m3_decode(codes)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+def test_fp8_forward_is_attention_on_dequantised_inputs():
+    # the codes' values times their descales, through PyTorch float64 SDPA
+    import synth as sy
+    from oracle import e4m3_decode, fp8_forward
+    x = [rnd(150 + i, 1, 2, 40, 16) for i in range(3)]
+    (q8, dq), (k8, dk), (v8, dv) = (sy.e4m3_codes(t) for t in x)
+    o, lse = fp8_forward(q8.numpy(), k8.numpy(), v8.numpy(), dq, dk, dv, 0.25,
+                         window_mask(40, 40, -1, 0))
+    qd, kd, vd = (e4m3_decode(c.numpy()) * s for c, s in ((q8, dq), (k8, dk), (v8, dv)))
+    ref = torch_sdpa(qd, kd, vd, 0.25, window_mask(40, 40, -1, 0)).numpy()
+    assert np.abs(o - ref).max() < 1e-12
+    # quantisation: every code is within half an E4M3 step of its scaled value
+    for t, (c, s) in zip(x, ((q8, dq), (k8, dk), (v8, dv))):
+        d = e4m3_decode(c.numpy())
+        assert (np.abs(d - t / s) <= np.maximum(np.abs(d) * 2.0 ** -4, 2.0 ** -10) + 1e-12).all()
