@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SDPA_VERSION 3
+#define SDPA_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum sdpa_status {
@@ -64,7 +64,9 @@ enum sdpa_status {
 };
 
 enum sdpa_layout { SDPA_LAYOUT_BSHD = 0, SDPA_LAYOUT_SBHD = 1, SDPA_LAYOUT_BHSD = 2, SDPA_LAYOUT_THD = 3 };
-enum sdpa_dtype { SDPA_DTYPE_F16 = 0, SDPA_DTYPE_BF16 = 1, SDPA_DTYPE_F32 = 2 };
+/* SDPA_DTYPE_FP8_E4M3: q, k, v as OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities), forward only, through sdpa_fwd_fp8; O is bf16. */
+enum sdpa_dtype { SDPA_DTYPE_F16 = 0, SDPA_DTYPE_BF16 = 1, SDPA_DTYPE_F32 = 2, SDPA_DTYPE_FP8_E4M3 = 3 };
 /* Where the diagonal of a window sits when seqlen_q != seqlen_k: query i is aligned with
  * key i (TOP_LEFT) or with key i + seqlen_k - seqlen_q (BOTTOM_RIGHT).  Per sequence for THD. */
 enum sdpa_diag_align { SDPA_ALIGN_TOP_LEFT = 0, SDPA_ALIGN_BOTTOM_RIGHT = 1 };
@@ -212,6 +214,25 @@ int sdpa_fwd_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdp
 int sdpa_fwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
              const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 forward ("[PyTorch] fused CUDNN attention kernel not properly handling strides",
+ * TransformerEngine issue 1195: its fused attention call carries an FP8 recipe,
+ * DelayedScaling, whose tensors are 8-bit codes with one fp32 scale per tensor).
+ * desc->dtype must be SDPA_DTYPE_FP8_E4M3: q, k, v hold E4M3 codes (strides in elements =
+ * bytes), o is bf16 with q's logical shape (its own strides, in bf16 elements), lse fp32.
+ * descale_q/k/v: DEVICE pointers to one fp32 each (NULL = 1.0); element values are
+ * code * descale.  Computes O = softmax(scale * Q K^T + mask) V on those values with both
+ * products on FP8 matrix cores; P is rounded to E4M3 after scaling by 2^8 (the row sum and
+ * the LSE use the unrounded fp32 P).  head_dim 64 or 128; q, k, v and o rows 16-byte aligned
+ * with k and v row strides >= head_dim (ERR_UNSUPPORTED otherwise); no block_mask.  The
+ * workspace is sdpa_fwd_workspace_size's.  Other calls reject SDPA_DTYPE_FP8_E4M3. */
+int sdpa_fwd_fp8_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                          const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                          size_t workspace_bytes);
+int sdpa_fwd_fp8(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                 const sdpa_tensor_t* v, const float* descale_q, const float* descale_k,
+                 const float* descale_v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward workspace size in bytes: fp32 Delta_i = dO_i . O_i - dLSE_i and fp32
  * LSE_i * log2(e) for every q row, plus the THD work lists.  Host only. */

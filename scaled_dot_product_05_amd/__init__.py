@@ -21,7 +21,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libsdpa.so")
 
 LAYOUTS = {"bshd": 0, "sbhd": 1, "bhsd": 2, "thd": 3}
-DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
+DTYPES = {"f16": 0, "bf16": 1, "f32": 2, "e4m3": 3}
 ALIGN = {"top_left": 0, "bottom_right": 1}
 
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_STRIDE", 4: "ERR_ALIGN",
@@ -77,6 +77,11 @@ _SIGNATURES = {
                           ctypes.c_int),
     "sdpa_fwd": ([_P(Desc)] + [_P(Tensor)] * 4 + [_P(RowStat), ctypes.c_void_p, ctypes.c_size_t,
                                                    ctypes.c_void_p], ctypes.c_int),
+    "sdpa_fwd_fp8_validate": ([_P(Desc)] + [_P(Tensor)] * 4 + [_P(RowStat), ctypes.c_size_t],
+                              ctypes.c_int),
+    "sdpa_fwd_fp8": ([_P(Desc)] + [_P(Tensor)] * 3 + [ctypes.c_void_p] * 3
+                     + [_P(Tensor), _P(RowStat), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
+                     ctypes.c_int),
     "sdpa_bwd_workspace_size": ([_P(Desc), _P(ctypes.c_size_t)], ctypes.c_int),
     "sdpa_bwd_validate": ([_P(Desc)] + [_P(Tensor)] * 4 + [_P(RowStat), _P(Tensor), _P(RowStat)]
                           + [_P(Tensor)] * 3 + [ctypes.c_size_t], ctypes.c_int),
@@ -142,7 +147,8 @@ def _check(status: int) -> None:
 
 def _dtype_name(t) -> str:
     import torch
-    return {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[t.dtype]
+    return {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
+            torch.float8_e4m3fn: "e4m3", torch.uint8: "e4m3"}[t.dtype]
 
 
 def tensor(t) -> Tensor:
@@ -245,6 +251,21 @@ def sdpa_fwd(desc, q, k, v, o, lse, workspace=None, stream=None) -> None:
     wp, wb = _ws(workspace)
     _check(lib().sdpa_fwd(ctypes.byref(desc), tensor(q), tensor(k), tensor(v), tensor(o),
                           rowstat(lse), wp, wb, _stream(stream)))
+
+
+def sdpa_fwd_fp8_validate(desc, q, k, v, o, lse, workspace_bytes: int = 0) -> None:
+    _check(lib().sdpa_fwd_fp8_validate(ctypes.byref(desc), tensor(q), tensor(k), tensor(v),
+                                       tensor(o), rowstat(lse), workspace_bytes))
+
+
+def sdpa_fwd_fp8(desc, q, k, v, descale_q, descale_k, descale_v, o, lse, workspace=None,
+                 stream=None) -> None:
+    """descale_*: device fp32 tensors of one element (None = 1.0)."""
+    wp, wb = _ws(workspace)
+    dp = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    _check(lib().sdpa_fwd_fp8(ctypes.byref(desc), tensor(q), tensor(k), tensor(v), dp(descale_q),
+                              dp(descale_k), dp(descale_v), tensor(o), rowstat(lse), wp, wb,
+                              _stream(stream)))
 
 
 def sdpa_bwd_validate(desc, q, k, v, o, lse, dout, dlse, dq, dk, dv, workspace_bytes: int) -> None:
@@ -402,6 +423,23 @@ def forward(q, k, v, layout: str, softmax_scale: float, window=(-1, -1), diag_al
     nws = sdpa_fwd_workspace_size(pr.desc)
     ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
     sdpa_fwd(pr.desc, q, k, v, o, l, ws, stream)
+    return o, l
+
+
+def forward_fp8(q, k, v, layout: str, softmax_scale: float, descale_q=None, descale_k=None,
+                descale_v=None, window=(-1, -1), diag_align="top_left", cu_seqlens_q=None,
+                cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None,
+                stream=None):
+    """Run sdpa_fwd_fp8 on E4M3 codes (torch uint8 or float8_e4m3fn tensors); descales are
+    device fp32 one-element tensors (None = 1).  Returns (O bf16 shaped like q, LSE fp32)."""
+    import torch
+    pr = Problem(q, k, layout, softmax_scale, window, diag_align, cu_seqlens_q, cu_seqlens_k,
+                 max_seqlen_q, max_seqlen_k)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty(pr.lse_shape, dtype=torch.float32, device=q.device) if lse is None else lse
+    nws = sdpa_fwd_workspace_size(pr.desc)
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    sdpa_fwd_fp8(pr.desc, q, k, v, descale_q, descale_k, descale_v, o, l, ws, stream)
     return o, l
 
 

@@ -52,7 +52,7 @@ bool debug_enabled() {
   return v == 1;
 }
 
-int esize_of(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? 4 : 2; }
+int esize_of(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? 4 : dtype == SDPA_DTYPE_FP8_E4M3 ? 1 : 2; }
 
 // A tensor normalised to (batch, head, row, d) order: extents, element strides, base.
 struct Norm {
@@ -229,7 +229,7 @@ int32_t clamp_rel(int64_t x) {
 int check_desc(const sdpa_desc_t* d, Shape* s) {
   if (!d) return fail(SDPA_ERR_NULL, "desc is NULL");
   if (d->layout < 0 || d->layout > SDPA_LAYOUT_THD) return fail(SDPA_ERR_ARG, "layout %d out of range", d->layout);
-  if (d->dtype < 0 || d->dtype > SDPA_DTYPE_F32) return fail(SDPA_ERR_ARG, "dtype %d out of range", d->dtype);
+  if (d->dtype < 0 || d->dtype > SDPA_DTYPE_FP8_E4M3) return fail(SDPA_ERR_ARG, "dtype %d out of range", d->dtype);
   if (d->diag_align != SDPA_ALIGN_TOP_LEFT && d->diag_align != SDPA_ALIGN_BOTTOM_RIGHT)
     return fail(SDPA_ERR_ARG, "diag_align %d out of range", d->diag_align);
   if (d->batch < 0 || d->seqlen_q < 0 || d->seqlen_k < 0)
@@ -388,12 +388,17 @@ int hip_fail(hipError_t e, const char* what) {
 // Validation shared by sdpa_fwd and sdpa_fwd_validate.
 int fwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
               const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
-              size_t ws_bytes, Attn* a, FwdParams* p) {
+              size_t ws_bytes, Attn* a, FwdParams* p, bool fp8 = false) {
   int rc = attn_setup(desc, a);
   if (rc) return rc;
+  if ((a->dtype == SDPA_DTYPE_FP8_E4M3) != fp8)
+    return fail(SDPA_ERR_UNSUPPORTED, fp8 ? "sdpa_fwd_fp8 needs dtype SDPA_DTYPE_FP8_E4M3"
+                                          : "FP8 inputs take sdpa_fwd_fp8 (forward only)");
+  if (fp8 && a->s.bm.bits) return fail(SDPA_ERR_UNSUPPORTED, "sdpa_fwd_fp8 takes no block_mask");
   if (!q || !k || !v || !o || !lse) return fail(SDPA_ERR_NULL, "a tensor handle is NULL");
   Norm nq = qlike(*a, "q", q), nk = klike(*a, "k", k), nv = klike(*a, "v", v);
-  Norm no = qlike(*a, "o", o);
+  // FP8: o is bf16
+  Norm no = fp8 ? make_tensor("o", o, a->layout, 2, a->nb, a->s.hq, a->rows_q, a->s.d) : qlike(*a, "o", o);
   Norm nl = statlike(*a, "lse", lse);
   bool has_lse = lse->data != nullptr;
   if ((rc = check_tensor(nq, false, true)) || (rc = check_tensor(nk, false, true)) ||
@@ -420,6 +425,10 @@ int fwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
   if (!has_lse) p->lse.ptr = nullptr;
   p->aligned = (aligned16(nq) ? kAlQ : 0) | (aligned16(nk) ? kAlK : 0) |
                (aligned16(nv) ? kAlV : 0) | (aligned16(no) ? kAlO : 0);
+  if (fp8 && !fwd8_ok(*p))
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "FP8 forward needs head_dim 64 or 128 and 16-byte aligned q/k/v/o rows with k/v "
+                "row strides >= head_dim");
   if (p->s.bm.bits && !fwd_block_mask_ok(*p, DType(a->dtype)))
     return fail(SDPA_ERR_UNSUPPORTED,
                 "block_mask needs 16-byte aligned q/k/v/o rows with k/v row strides >= head_dim "
@@ -434,6 +443,7 @@ int bwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
               BwdParams* p) {
   int rc = attn_setup(desc, a);
   if (rc) return rc;
+  if (a->dtype == SDPA_DTYPE_FP8_E4M3) return fail(SDPA_ERR_UNSUPPORTED, "FP8 inputs: forward only");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(SDPA_ERR_NULL, "a tensor handle is NULL");
   Norm nq = qlike(*a, "q", q), nk = klike(*a, "k", k), nv = klike(*a, "v", v);
@@ -497,6 +507,7 @@ int merge_setup(const sdpa_merge_desc_t* d, Merge* m) {
   if (!d) return fail(SDPA_ERR_NULL, "merge desc is NULL");
   if (d->layout < 0 || d->layout > SDPA_LAYOUT_THD) return fail(SDPA_ERR_ARG, "layout out of range");
   if (d->dtype < 0 || d->dtype > SDPA_DTYPE_F32) return fail(SDPA_ERR_ARG, "dtype out of range");
+  if (d->dtype == SDPA_DTYPE_FP8_E4M3) return fail(SDPA_ERR_UNSUPPORTED, "the merge takes fp16, bf16 or fp32");
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
     return fail(SDPA_ERR_UNSUPPORTED, "head_dim %d not built (32, 64, 128)", d->head_dim);
   m->thd = d->layout == SDPA_LAYOUT_THD;
@@ -672,6 +683,50 @@ int sdpa_fwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     p.work_count = count;
   }
   if ((e = launch_fwd(p, DType(a.dtype), st)) != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
+int sdpa_fwd_fp8_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                          const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                          size_t workspace_bytes) {
+  Attn a;
+  FwdParams p;
+  int rc = fwd_check(desc, q, k, v, o, lse, workspace_bytes, &a, &p, true);
+  return rc ? rc : ok();
+}
+
+int sdpa_fwd_fp8(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                 const sdpa_tensor_t* v, const float* descale_q, const float* descale_k,
+                 const float* descale_v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  Attn a;
+  FwdParams p;
+  int rc = fwd_check(desc, q, k, v, o, lse, workspace_bytes, &a, &p, true);
+  if (rc) return rc;
+  size_t need = fwd_ws_bytes(a.s, a.dtype);
+  if (need && !workspace) return fail(SDPA_ERR_WORKSPACE, "THD forward needs a workspace");
+  p.descale_q = descale_q;
+  p.descale_k = descale_k;
+  p.descale_v = descale_v;
+  debug_log("fwd_fp8", a, &p.aligned);
+  if (a.s.batch == 0 || a.rows_q == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (a.s.thd) {
+    char* ws = static_cast<char*>(workspace);
+    const int bm = fwd_rows_per_tile(a.dtype);
+    int64_t nitems = thd_items(a.s.total_q, a.s.batch, bm);
+    WorkItem* items = reinterpret_cast<WorkItem*>(ws);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + need - 256);
+    SchedParams sp = sched_params(a.s, true, items, count);
+    sp.tile_own = bm;
+    sp.tile_other = kFwdBN16;
+    sp.max_items = int32_t(nitems);
+    if ((e = launch_schedule(sp, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
+    p.work = items;
+    p.work_count = count;
+  }
+  if ((e = launch_fwd8(p, st)) != hipSuccess) return hip_fail(e, "FP8 forward launch");
   return ok();
 }
 

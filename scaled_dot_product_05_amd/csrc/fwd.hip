@@ -1015,6 +1015,310 @@ static hipError_t fwd16_dispatch(const FwdParams& p, hipStream_t st) {
   }
 }
 
+// ----------------------------------------------------------------------------------------
+// FP8 (E4M3) inputs, bf16 output.  "[PyTorch] fused CUDNN attention kernel not properly
+// handling strides" (TransformerEngine issue 1195) hands its fused attention an FP8 recipe
+// (DelayedScaling): tensors as 8-bit codes with one fp32 scale each, value = code *
+// descale.  Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit
+// block scales, 64-deep contraction).  That instruction pairs byte idx of an A lane with
+// byte idx of the B lane in the same half of the wave, so each operand only has to agree on
+// which key or d each (half, byte) holds:
+//   Q K^T: A = K rows, B = Q rows, byte idx of half h = d 64 e + 32 h + idx;
+//   P V:   B = P^T straight from the score registers (byte 16 k2 + r = register r of key
+//          block k2, i.e. key 32 k2 + 8 (r / 4) + 4 h + r % 4), A = V^T gathered in that key
+//          order by ds_read_b64_tr_b8 (lane 16g + 8a + b receives byte b of the rows the
+//          lanes 16g + a + 2c address, c = 0..7): four reads of 8 bytes per 32 columns.
+// The softmax takes the exact running max every tile, so P is in [0, 1]; it is scaled by
+// 2^8 (added to the exponent) so that P * 256 uses E4M3's normal range down to 2^-14, and
+// the row sum carries the same factor (O unaffected, LSE takes -8).
+// ----------------------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16_t mfma_e4m3(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x2_t read_tr8(const lds_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)p);
+}
+
+// V rows of an FP8 tile: 16-byte chunk c of row r sits at slot c ^ swv8(r).  With it the
+// eight rows × two chunks one transposed read touches per 32 lanes fall on 64 distinct
+// banks (checked on the CPU for D 64 and 128).
+template <int CPR>
+__device__ __forceinline__ int swv8(int r) {
+  return CPR == 4 ? ((r & 1) | (((r >> 3) & 1) << 1))
+                  : ((r & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2));
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd8_kernel(FwdParams p) {
+  constexpr int BM = 32 * kWaves, BN = 64;
+  constexpr int CPR = D / 16;                 // 16-byte chunks per row
+  constexpr int TB = BN * D;                  // bytes per K or V tile
+  constexpr int NDMA = BN * CPR / kThreads;   // 16-byte loads per thread per tile
+  constexpr int NE = D / 64;                  // 64-deep contraction blocks of Q K^T
+  constexpr int NDB = D / 32;                 // 32-column blocks of O
+  constexpr int NS = 3;                       // K and V slots each
+  static_assert(NDMA >= 1 && (D == 64 || D == 128), "tile split");
+  __shared__ __align__(16) char smem_[2 * NS * TB];
+  lds_t* const lds = (lds_t*)smem_;
+
+  const Shape& s = p.s;
+  WorkPos w;
+  if (!decode_work(p, BM, w)) return;
+  const Seq g = seq_of(s, w.b);
+  const int q0 = w.tile * BM;
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BM, g.sq);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hk = w.h / s.group;
+  const uint8_t* qb = static_cast<const uint8_t*>(p.q.ptr) + w.b * p.q.sb + w.h * p.q.sh + g.qrow0 * p.q.ss;
+  const uint8_t* kb = static_cast<const uint8_t*>(p.k.ptr) + w.b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint8_t* vb = static_cast<const uint8_t*>(p.v.ptr) + w.b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint16_t* ob = static_cast<uint16_t*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN;
+  const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  const int qw0 = q0 + wave * 32;
+  const int qw1 = min(qw0 + 32, g.sq);
+  int wf0 = 0, wf1 = 0;  // key tiles every row of this wave sees in full
+  if (qw0 < qw1) {
+    const int64_t lo_full = int64_t(qw1 - 1) + g.off + s.lo_rel;
+    const int64_t hi_full = min(int64_t(qw0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
+    const int64_t a = lo_full <= 0 ? 0 : (lo_full + BN - 1) / BN;
+    const int64_t b = hi_full < 0 ? 0 : (hi_full + 1) / BN;
+    wf0 = int(clamp64(a, 0, int64_t(1) << 30));
+    wf1 = int(clamp64(b, wf0, int64_t(1) << 30));
+  }
+
+  // descales and the score multiplier in log2 units; a negative product flips q's signs
+  const float dsq = p.descale_q ? *p.descale_q : 1.f;
+  const float dsk = p.descale_k ? *p.descale_k : 1.f;
+  const float dsv = p.descale_v ? *p.descale_v : 1.f;
+  const float craw = s.scale_log2 * dsq * dsk;
+  const float c = fmaxf(fabsf(craw), 1e-30f);
+  const uint32_t qsign = craw < 0.f ? 0x80808080u : 0u;
+
+  // Q fragments: lane (query l32, half hf) holds d = 64 e + 32 hf + 0..31 of its row
+  i32x8_t qf[NE];
+  {
+    const int qr = min(qw0 + l32, g.sq - 1);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const uint4* src = reinterpret_cast<const uint4*>(qb + int64_t(qr) * p.q.ss + 64 * e + 32 * hf);
+      const uint4 x0 = src[0], x1 = src[1];
+      qf[e] = i32x8_t{int(x0.x ^ qsign), int(x0.y ^ qsign), int(x0.z ^ qsign), int(x0.w ^ qsign),
+                      int(x1.x ^ qsign), int(x1.y ^ qsign), int(x1.z ^ qsign), int(x1.w ^ qsign)};
+    }
+  }
+
+  // ---- HBM -> LDS (rows past the sequence end read as zeros) ----
+  const int64_t kss = p.k.ss, vss = p.v.ss;
+  uint32_t koff_g[NDMA], voff_g[NDMA];
+#pragma unroll
+  for (int u = 0; u < NDMA; ++u) {
+    const int P = (u * kWaves + wave) * 64 + lane;
+    const int row = P / CPR, pos = P % CPR;
+    koff_g[u] = uint32_t(row * kss + ((pos ^ swk<CPR>(row)) * 16));
+    voff_g[u] = uint32_t(row * vss + ((pos ^ swv8<CPR>(row)) * 16));
+  }
+  const i32x4_t rk = make_rsrc(kb, (int64_t(g.sk) - 1) * kss + D);
+  const i32x4_t rv = make_rsrc(vb, (int64_t(g.sk) - 1) * vss + D);
+  const uint32_t kstep = uint32_t(BN * kss), vstep = uint32_t(BN * vss);
+  auto issue_k = [&](int t, int slot) {
+    const uint32_t o = uint32_t(t) * kstep;
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rk, lds + slot * TB + (u * kWaves + wave) * 1024, koff_g[u] + o);
+  };
+  auto issue_v = [&](int t, int slot) {
+    const uint32_t o = uint32_t(t) * vstep;
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rv, lds + (NS + slot) * TB + (u * kWaves + wave) * 1024, voff_g[u] + o);
+  };
+
+  // ---- LDS operand offsets (lane part) ----
+  int ka[NE][2];
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+      ka[e][part] = l32 * D + (((4 * e + 2 * hf + part) ^ swk<CPR>(l32)) * 16);
+  int va[NDB][4];
+  {
+    const int g4 = lane >> 4, a = lane & 1, cc = (lane & 15) >> 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = 16 * j + 8 * (cc >> 2) + 4 * (g4 >> 1) + (cc & 3);
+        const int unit = 2 * db + (g4 & 1);
+        va[db][j] = key * D + ((unit ^ swv8<CPR>(key)) * 16) + 8 * a;
+      }
+  }
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+  float m_run = kNegInf, l_run = 0.f;
+
+  // S^T of the K tile in slot sl: two 32-key blocks, NE MFMAs each
+  auto scores = [&](int sl, f32x16_t(&st)[2]) {
+    const lds_t* base = lds + sl * TB;
+    st[0] = zero16();
+    st[1] = zero16();
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint4 a0 = lds_read16(base + k2 * 32 * D + ka[e][0]);
+        const uint4 a1 = lds_read16(base + k2 * 32 * D + ka[e][1]);
+        const i32x8_t a = {int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
+        st[k2] = mfma_e4m3(a, qf[e], st[k2]);
+      }
+  };
+  auto pv = [&](int sl, const i32x8_t& pf) {
+    const lds_t* base = lds + (NS + sl) * TB;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const i32x2_t r0 = read_tr8(base + va[db][0]), r1 = read_tr8(base + va[db][1]);
+      const i32x2_t r2 = read_tr8(base + va[db][2]), r3 = read_tr8(base + va[db][3]);
+      const i32x8_t a = {r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+      acc[db] = mfma_e4m3(a, pf, acc[db]);
+    }
+  };
+  // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
+  auto mask = [&](int t, f32x16_t(&st)[2]) {
+    if (t < wf0 || t >= wf1) {
+      asm volatile("" ::: "memory");
+      const int qi = qw0 + l32;
+      const int base_rel = t * BN - qi - g.off + 4 * hf;
+      const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = base_rel + k2 * 32 + 8 * (r >> 2) + (r & 3);
+          st[k2][r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[k2][r] : kNegInf;
+        }
+    }
+  };
+  // exact running max, P * 256 packed to E4M3 as the B operand of P V
+  auto softmax = [&](const f32x16_t(&st)[2], i32x8_t& pf) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[k2][r]);
+    mx = max_halves(mx);
+    const float m_tile = mx == kNegInf ? kNegInf : mx * c;
+    const float m_new = fmaxf(m_run, m_tile);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float off = 8.f - (m_run == kNegInf ? 0.f : m_run);
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      const int k2 = wd >> 2, rb = 4 * (wd & 3);
+      const float e0 = fast_exp2(__builtin_fmaf(st[k2][rb], c, off));
+      const float e1 = fast_exp2(__builtin_fmaf(st[k2][rb + 1], c, off));
+      const float e2 = fast_exp2(__builtin_fmaf(st[k2][rb + 2], c, off));
+      const float e3 = fast_exp2(__builtin_fmaf(st[k2][rb + 3], c, off));
+      ps0 += e0 + e1;
+      ps1 += e2 + e3;
+      pf[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false), true);
+    }
+    l_run += ps0 + ps1;
+  };
+
+  // Slots: K(t) and V(t) in slot t % 3.  Step t reads K(t+1) and V(t), issues the loads of
+  // K(t+3) and V(t+2) and waits, before its barrier, for all loads but its own.
+  const int n = kt1 - kt0;
+  f32x16_t sa[2], sb[2];
+  if (n > 0) {
+    issue_k(kt0, 0);
+    issue_v(kt0, 0);
+    issue_k(kt0 + 1, 1);
+    issue_v(kt0 + 1, 1);
+    issue_k(kt0 + 2, 2);
+    vm_wait<2 * NDMA>();
+    lds_barrier();
+    scores(0, sa);
+    lds_barrier();  // step 0 reloads K slot 0
+  }
+  int ph = 0;
+  for (int i = 0; i < n; ++i) {
+    const int t = kt0 + i;
+    const int p1 = ph == NS - 1 ? 0 : ph + 1, p2 = p1 == NS - 1 ? 0 : p1 + 1;
+    issue_k(t + NS, ph);
+    issue_v(t + NS - 1, p2);
+    mask(t, sa);
+    scores(p1, sb);  // past the last tile: zeros, unused
+    i32x8_t pf;
+    softmax(sa, pf);
+    pv(ph, pf);
+    vm_wait<2 * NDMA>();
+    lds_barrier();
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+    ph = p1;
+  }
+  vm_wait<0>();  // no load may land in LDS after the workgroup ends
+
+  const float lt = sum_halves(l_run);
+  const int qi = qw0 + l32;
+  if (qi < g.sq) {
+    const float inv = lt > 0.f ? dsv / lt : 0.f;
+    uint16_t* orow = ob + int64_t(qi) * p.o.ss;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = db * 32 + 8 * gq + 4 * hf;
+        const uint32_t lo = pack2<true>(acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv);
+        const uint32_t hi = pack2<true>(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo, hi);
+      }
+    if (hf == 0 && p.lse.ptr) {
+      float* lp = p.lse.ptr + w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
+      *lp = lt > 0.f ? (m_run + __log2f(lt) - 8.f) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// The FP8 kernel needs 16-byte aligned rows of q, k, v and o, k/v row strides of at least
+// D bytes and 32-bit tile offsets (as the pipelined 16-bit kernel).
+bool fwd8_ok(const FwdParams& p) {
+  constexpr int need = kAlQ | kAlK | kAlV | kAlO;
+  const int64_t kv_ss = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
+  return (p.s.d == 64 || p.s.d == 128) && (p.aligned & need) == need && p.k.ss >= p.s.d &&
+         p.v.ss >= p.s.d && (int64_t(p.s.sk) + 4 * 64) * kv_ss < (int64_t(1) << 31);
+}
+
+hipError_t launch_fwd8(const FwdParams& p, hipStream_t st) {
+  const int64_t blocks = fwd_grid(p, 32 * kWaves);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  prof_begin(st, "attn_fwd_fp8");
+  if (p.s.d == 64)
+    hipLaunchKernelGGL(fwd8_kernel<64>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(fwd8_kernel<128>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  prof_end(st);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdParams& p, DType dt, hipStream_t st) {
   const Shape& s = p.s;
   if (dt == DType::BF16) return fwd16_dispatch<true>(p, st);

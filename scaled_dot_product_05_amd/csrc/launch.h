@@ -8,6 +8,9 @@ namespace sdpa {
 
 hipError_t launch_schedule(const SchedParams& p, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, DType dtype, hipStream_t stream);
+// FP8 (E4M3) q, k, v with per-tensor descales, bf16 O
+hipError_t launch_fwd8(const FwdParams& p, hipStream_t stream);
+bool fwd8_ok(const FwdParams& p);
 hipError_t launch_bwd(const BwdParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_merge_fwd(const MergeParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_merge_bwd(const MergeParams& p, DType dtype, hipStream_t stream);

@@ -6,7 +6,7 @@
 
 namespace sdpa {
 
-enum class DType : int32_t { F16 = 0, BF16 = 1, F32 = 2 };
+enum class DType : int32_t { F16 = 0, BF16 = 1, F32 = 2, E4M3 = 3 };
 
 // Strided [batch, head, row, d] view.  For packed varlen (THD) tensors sb is 0 and a
 // row index is the packed row t = cu_seqlens[b] + i.
@@ -74,6 +74,9 @@ struct FwdParams {
   const WorkItem* work;  // THD: longest-first list of (seq, q tile)
   const int32_t* work_count;
   int32_t aligned;
+  const float* descale_q;  // FP8 inputs: value = code * descale (null: 1)
+  const float* descale_k;
+  const float* descale_v;
 };
 
 struct BwdParams {

@@ -26,11 +26,11 @@ def header_functions():
 def test_every_declared_symbol_is_exported_and_bound():
     lib = S.lib()
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.exported_symbols())
-    assert S.sdpa_version() == 3
+    assert S.sdpa_version() == 4
 
 
 def status_of(fn, *args):
@@ -287,3 +287,34 @@ def test_block_mask_build_rejects_bad_arguments():
     bad = _FakeMask(1, 1)
     bad.desc.bits = None
     assert status_of(S.sdpa_block_mask_build, bad.desc, 64, 64) == "ERR_NULL"
+
+
+def test_fp8_validation_on_host():
+    b, s_, h, d = 1, 256, 4, 64
+    q = torch.zeros(b, s_, h, d, dtype=torch.uint8)
+    k, v = q.clone(), q.clone()
+    o = torch.zeros(b, s_, h, d, dtype=torch.bfloat16)
+    lse = torch.zeros(b, h, s_, dtype=torch.float32)
+    desc = S.make_desc("bshd", "e4m3", b, s_, s_, h, h, d, 0.125, (-1, 0))
+    assert status_of(S.sdpa_fwd_fp8_validate, desc, q, k, v, o, lse) == "OK"
+    # the other entry points take no FP8
+    assert fwd_status(desc, q, k, v, o, lse) == "ERR_UNSUPPORTED"
+    ws = S.sdpa_bwd_workspace_size(desc)
+    assert status_of(S.sdpa_bwd_validate, desc, q, k, v, o, lse, o, None, q.clone(), k.clone(),
+                     v.clone(), ws) == "ERR_UNSUPPORTED"
+    # fp16 / bf16 / fp32 descriptors do not take the FP8 call
+    d16 = S.make_desc("bshd", "bf16", b, s_, s_, h, h, d, 0.125, (-1, 0))
+    assert status_of(S.sdpa_fwd_fp8_validate, d16, q, k, v, o, lse) == "ERR_UNSUPPORTED"
+    # head_dim 32, unaligned rows
+    d32 = S.make_desc("bshd", "e4m3", b, s_, s_, h, h, 32, 0.125, (-1, 0))
+    q32 = torch.zeros(b, s_, h, 32, dtype=torch.uint8)
+    o32 = torch.zeros(b, s_, h, 32, dtype=torch.bfloat16)
+    assert status_of(S.sdpa_fwd_fp8_validate, d32, q32, q32.clone(), q32.clone(), o32,
+                     lse) == "ERR_UNSUPPORTED"
+    big = torch.zeros(b, s_, h, d + 8, dtype=torch.uint8)
+    assert status_of(S.sdpa_fwd_fp8_validate, desc, big[..., 8:], k, v, o, lse) == "ERR_UNSUPPORTED"
+    # O (bf16) over the bytes of an input
+    buf = torch.zeros(b, s_, h, 2 * d, dtype=torch.uint8)
+    qa = buf[..., :d]
+    oa = buf.view(torch.bfloat16)
+    assert status_of(S.sdpa_fwd_fp8_validate, desc, qa, k, v, oa, lse) == "ERR_ALIAS"
