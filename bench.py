@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of gfx950 MFMA peak per dtype"
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA, MI355X
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8": 5033.2}  # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {  # which source file holds each kernel (for the traffic-staleness check)
@@ -281,6 +281,7 @@ def extra(torch, S, synth, dev):
                               "bwd_TFLOP/s": round(10 * 128 * nvis / (msb * 1e-3) / 1e12, 2)}
 
     res["block_sparse_bf16"] = block_sparse(torch, S, synth, dev)
+    res["fp8_e4m3_fwd"] = fp8_forward(torch, S, synth, dev)
 
     # merge kernels, HBM bound: x [4,16,8192,128] fp32, lse [4,16,8192]
     mg = {}
@@ -367,6 +368,40 @@ def block_sparse(torch, S, synth, dev):
                      f"{native}_bwd_TFLOP/s": tf(10 * d * nvis, msnb)}
         log(f"block mask {name}: build {ms_build:.3f} ms fwd {msf:.3f} ms bwd {msb:.3f} ms; "
             f"{native} fwd {msnf:.3f} ms bwd {msnb:.3f} ms")
+    return out
+
+
+def fp8_forward(torch, S, synth, dev):
+    """FP8 (E4M3) forward: causal at long S (TFLOP/s against the FP8 and the bf16 MFMA
+    peaks) and non-causal short sequences (bytes: q, k, v codes read once, bf16 O and fp32
+    LSE written once)."""
+    out = {"causal": [], "short_seq": []}
+    for (b, s, h, d) in [(8, 4096, 8, 64), (2, 16384, 8, 64), (8, 4096, 16, 128)]:
+        w = synth.target(b=b, s=s, h=h, d=d)
+        codes = [synth.e4m3_codes(synth.f64(t)) for t in (w.q, w.k, w.v)]
+        q, k, v = (c.to(dev) for c, _ in codes)
+        ds = [torch.tensor([x], dtype=torch.float32, device=dev) for _, x in codes]
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(b, h, s, dtype=torch.float32, device=dev)
+        ms = time_calls(torch, lambda: S.forward_fp8(q, k, v, "bshd", w.scale, *ds, window=(-1, 0),
+                                                     out=o, lse=lse))
+        tf = 4 * d * (b * h * s * (s + 1) // 2) / (ms * 1e-3) / 1e12
+        out["causal"].append({"B": b, "S": s, "H": h, "D": d, "fwd_ms": round(ms, 4),
+                              "TFLOP/s": round(tf, 2),
+                              "frac_fp8_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
+                              "frac_bf16_peak": round(tf / PEAK_TFLOPS["bf16"], 4)})
+        log(f"fp8 fwd B{b} S{s} H{h} D{d}: {ms:.3f} ms {tf:.1f} TFLOP/s")
+        del q, k, v, o, lse
+    for s in (128, 512):
+        b = (1 << 21) // (16 * s)
+        q, k, v = (torch.randn(b, s, 16, 64, device=dev).to(torch.float8_e4m3fn) for _ in range(3))
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(b, 16, s, device=dev)
+        ms = time_calls(torch, lambda: S.forward_fp8(q, k, v, "bshd", 0.125, out=o, lse=lse))
+        nbytes = 3 * q.numel() + 2 * o.numel() + 4 * lse.numel()
+        out["short_seq"].append({"S": s, "B": b, "H": 16, "D": 64, "ms": round(ms, 4),
+                                 "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        del q, k, v, o, lse
     return out
 
 
