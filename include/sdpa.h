@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SDPA_VERSION 4
+#define SDPA_VERSION 5
 
 /* Status codes returned by every entry point. */
 enum sdpa_status {
@@ -181,7 +181,11 @@ typedef struct sdpa_desc {
 } sdpa_desc_t;
 
 /* Merge description: rows of x are [layout order] tensors of `heads` heads of head_dim,
- * lse is the matching row statistic.  THD uses `total` rows and ignores batch/seqlen. */
+ * lse is the matching row statistic.  THD uses `total` rows and ignores seqlen; with
+ * cu_seqlens (THD only, optional, DEVICE int32[batch+1]) only the rows of the batch sequences
+ * are merged: sequence b's rows start at cu_seqlens_padded[b] (DEVICE int32[batch+1], or
+ * cu_seqlens[b] when NULL) and number cu_seqlens[b+1] - cu_seqlens[b]; other rows are not
+ * touched.  Entries are clamped to [0, total] on the device. */
 typedef struct sdpa_merge_desc {
   int32_t layout;
   int32_t dtype;
@@ -190,6 +194,8 @@ typedef struct sdpa_merge_desc {
   int32_t heads;
   int32_t head_dim;
   int64_t total;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens_padded;
 } sdpa_merge_desc_t;
 
 /* Library version (SDPA_VERSION of the build). */

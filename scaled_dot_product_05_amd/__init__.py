@@ -65,7 +65,8 @@ class Desc(ctypes.Structure):
 class MergeDesc(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("seqlen", ctypes.c_int32), ("heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("total", ctypes.c_int64)]
+                ("head_dim", ctypes.c_int32), ("total", ctypes.c_int64),
+                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_padded", ctypes.c_void_p)]
 
 
 _P = ctypes.POINTER
@@ -196,8 +197,12 @@ def make_desc(layout: str, dtype: str, batch: int, seqlen_q: int, seqlen_k: int,
 
 
 def make_merge_desc(layout: str, dtype: str, batch: int, seqlen: int, heads: int, head_dim: int,
-                    total: int = 0) -> MergeDesc:
-    return MergeDesc(LAYOUTS[layout], DTYPES[dtype], batch, seqlen, heads, head_dim, total)
+                    total: int = 0, cu_seqlens=None, cu_seqlens_padded=None) -> MergeDesc:
+    """cu_seqlens / cu_seqlens_padded: optional device int32 tensors (THD: merge only the rows
+    of these sequences, at their padded starts)."""
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    return MergeDesc(LAYOUTS[layout], DTYPES[dtype], batch, seqlen, heads, head_dim, total,
+                     ptr(cu_seqlens), ptr(cu_seqlens_padded))
 
 
 # ---------------------------------------------------------------------------------------
@@ -492,11 +497,13 @@ def merge_backward(x_a, lse_a, x_b, lse_b, g, g_lse, layout: str, stream=None):
 
 
 def cp_forward(q, k, v, layout: str, softmax_scale: float, window, cp: int, hop_order=None,
-               stream=None):
-    """Run sdpa_cp_fwd (context-parallel ring emulated on one GPU); returns (O, LSE)."""
+               stream=None, cu_seqlens=None, max_seqlen=None, cu_seqlens_padded=None, out=None):
+    """Run sdpa_cp_fwd (context-parallel ring emulated on one GPU); returns (O, LSE).  THD:
+    cu_seqlens (shared by q and k), max_seqlen and optional cu_seqlens_padded."""
     import torch
-    pr = Problem(q, k, layout, softmax_scale, window)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format)
+    pr = Problem(q, k, layout, softmax_scale, window, "top_left", cu_seqlens, cu_seqlens,
+                 max_seqlen, max_seqlen, cu_seqlens_padded, cu_seqlens_padded)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     l = torch.empty(pr.lse_shape, dtype=torch.float32, device=q.device)
     ws = torch.empty(sdpa_cp_workspace_size(pr.desc, cp), dtype=torch.uint8, device=q.device)
     sdpa_cp_fwd(pr.desc, cp, hop_order, q, k, v, o, l, ws, stream)
@@ -504,13 +511,15 @@ def cp_forward(q, k, v, layout: str, softmax_scale: float, window, cp: int, hop_
 
 
 def cp_backward(q, k, v, o, lse, dout, layout: str, softmax_scale: float, window, cp: int,
-                hop_order=None, dlse=None, stream=None):
+                hop_order=None, dlse=None, stream=None, cu_seqlens=None, max_seqlen=None,
+                cu_seqlens_padded=None, dq=None, dk=None, dv=None):
     """Run sdpa_cp_bwd; returns (dQ, dK, dV)."""
     import torch
-    pr = Problem(q, k, layout, softmax_scale, window)
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    pr = Problem(q, k, layout, softmax_scale, window, "top_left", cu_seqlens, cu_seqlens,
+                 max_seqlen, max_seqlen, cu_seqlens_padded, cu_seqlens_padded)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     ws = torch.empty(sdpa_cp_workspace_size(pr.desc, cp), dtype=torch.uint8, device=q.device)
     sdpa_cp_bwd(pr.desc, cp, hop_order, q, k, v, o, lse, dout, dlse, dq, dk, dv, ws, stream)
     return dq, dk, dv

@@ -501,12 +501,15 @@ struct Merge {
   int64_t nb, h, rows, d;
   int32_t layout, dtype;
   bool thd;
+  const int32_t* cu = nullptr;   // THD sequence map (optional)
+  const int32_t* pad = nullptr;
+  int32_t nseq = 0;
 };
 
 int merge_setup(const sdpa_merge_desc_t* d, Merge* m) {
   if (!d) return fail(SDPA_ERR_NULL, "merge desc is NULL");
   if (d->layout < 0 || d->layout > SDPA_LAYOUT_THD) return fail(SDPA_ERR_ARG, "layout out of range");
-  if (d->dtype < 0 || d->dtype > SDPA_DTYPE_F32) return fail(SDPA_ERR_ARG, "dtype out of range");
+  if (d->dtype < 0 || d->dtype > SDPA_DTYPE_FP8_E4M3) return fail(SDPA_ERR_ARG, "dtype out of range");
   if (d->dtype == SDPA_DTYPE_FP8_E4M3) return fail(SDPA_ERR_UNSUPPORTED, "the merge takes fp16, bf16 or fp32");
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
     return fail(SDPA_ERR_UNSUPPORTED, "head_dim %d not built (32, 64, 128)", d->head_dim);
@@ -514,9 +517,17 @@ int merge_setup(const sdpa_merge_desc_t* d, Merge* m) {
   if (d->heads < 1 || d->heads > 65535) return fail(SDPA_ERR_SHAPE, "heads=%d", d->heads);
   if (m->thd) {
     if (d->total < 0 || d->total > INT32_MAX) return fail(SDPA_ERR_SHAPE, "total out of range");
+    if (d->cu_seqlens && d->batch < 0) return fail(SDPA_ERR_SHAPE, "batch out of range");
+    if (!d->cu_seqlens && d->cu_seqlens_padded)
+      return fail(SDPA_ERR_NULL, "cu_seqlens_padded without cu_seqlens");
   } else if (d->batch < 0 || d->seqlen < 0 || d->seqlen > kMaxSeqlen) {
     return fail(SDPA_ERR_SHAPE, "batch/seqlen out of range");
+  } else if (d->cu_seqlens || d->cu_seqlens_padded) {
+    return fail(SDPA_ERR_ARG, "cu_seqlens in a merge are for the THD layout only");
   }
+  m->cu = m->thd ? d->cu_seqlens : nullptr;
+  m->pad = m->thd ? d->cu_seqlens_padded : nullptr;
+  m->nseq = d->batch;
   m->layout = d->layout;
   m->dtype = d->dtype;
   m->nb = m->thd ? 1 : d->batch;
@@ -541,6 +552,9 @@ void merge_params(const Merge& m, MergeParams* p) {
   p->heads = int32_t(m.h);
   p->d = int32_t(m.d);
   p->thd = m.thd;
+  p->cu = m.cu;
+  p->pad = m.pad;
+  p->nseq = m.cu ? m.nseq : 0;
 }
 
 int merge_fwd_check(const sdpa_merge_desc_t* desc, const sdpa_tensor_t* xa,

@@ -13,14 +13,24 @@
 // of full attention, so each pair's sdpa_bwd adds exactly its share of dQ, dK, dV.  Each
 // chunk's diagonal pair writes first (accumulate = 0); every other pair adds in hop order.
 //
-// Host orchestration only: every step is an sdpa_fwd / sdpa_merge_fwd / sdpa_bwd launch.
+// THD (the page's own case): chunk c of every sequence at once is a padded-THD view of the
+// same tensors (per-sequence row starts and chunk lengths, built on the device by
+// launch_cp_chunks; sequences of any length, chunk lengths differing by at most one), and
+// the partial results live in full-size packed buffers at the same rows, folded by the merge
+// restricted to those rows.
+//
+// Host orchestration only: every step is an sdpa_fwd / sdpa_merge_fwd / sdpa_bwd launch (and,
+// for THD, one launch that builds the chunk views).
 #include <stdint.h>
 #include <string.h>
 
 #include <string>
 #include <vector>
 
+#include <hip/hip_runtime_api.h>
+
 #include "../../include/sdpa.h"
+#include "launch.h"
 
 namespace sdpa {
 int set_error(int code, const char* msg);
@@ -39,28 +49,40 @@ int seq_dim(int32_t layout) { return layout == SDPA_LAYOUT_SBHD ? 0 : layout == 
 struct Plan {
   sdpa_desc_t chunk;  // one chunk against one chunk
   int cp = 0, len = 0, esize = 0;
+  bool thd = false;
   std::vector<int> order;  // hop h -> ring distance
-  int64_t part_x = 0, part_l = 0;  // bytes of a chunk-sized O and LSE
+  int64_t part_x = 0, part_l = 0;  // bytes of a chunk-sized O and LSE (THD: full-size)
+  // THD workspace: chunk views, then the fold buffers, then the attention calls' workspace
+  int64_t views = 0, attn_off = 0;
+  size_t attn_bytes = 0;
 };
 
 int plan(const sdpa_desc_t* d, int cp, const int32_t* hop_order, Plan& p) {
   if (!d) return sdpa::set_error(SDPA_ERR_NULL, "descriptor is NULL");
   if (cp < 1 || cp > kMaxCp) return sdpa::set_error(SDPA_ERR_ARG, "cp must be in [1, 64]");
-  if (d->layout == SDPA_LAYOUT_THD)
-    return sdpa::set_error(SDPA_ERR_UNSUPPORTED, "context-parallel emulation supports BSHD, SBHD and BHSD");
-  if (d->layout < 0 || d->layout > SDPA_LAYOUT_BHSD) return sdpa::set_error(SDPA_ERR_ARG, "bad layout");
+  if (d->layout < 0 || d->layout > SDPA_LAYOUT_THD) return sdpa::set_error(SDPA_ERR_ARG, "bad layout");
+  const bool thd = d->layout == SDPA_LAYOUT_THD;
+  if (thd && (d->cu_seqlens_q != d->cu_seqlens_k || d->total_q != d->total_k ||
+              d->cu_seqlens_q_padded != d->cu_seqlens_k_padded))
+    return sdpa::set_error(SDPA_ERR_UNSUPPORTED,
+                           "context-parallel THD is self-attention: q and k share cu_seqlens (and padded starts)");
+  if (thd && (!d->cu_seqlens_q || d->batch < 0))
+    return sdpa::set_error(SDPA_ERR_NULL, "THD needs cu_seqlens");
   if (d->block_mask)
     return sdpa::set_error(SDPA_ERR_UNSUPPORTED, "context-parallel emulation takes no block_mask");
   if (d->seqlen_q != d->seqlen_k)
     return sdpa::set_error(SDPA_ERR_SHAPE, "context-parallel emulation needs seqlen_q == seqlen_k");
-  if (d->seqlen_q <= 0 || d->seqlen_q % (2 * cp) != 0)
+  if (!thd && (d->seqlen_q <= 0 || d->seqlen_q % (2 * cp) != 0))
     return sdpa::set_error(SDPA_ERR_SHAPE, "seqlen must be a positive multiple of 2 * cp");
   const bool causal = d->window_left == -1 && d->window_right == 0;
   const bool full = d->window_left == -1 && d->window_right == -1;
   if (!causal && !full)
     return sdpa::set_error(SDPA_ERR_UNSUPPORTED, "context-parallel emulation supports causal (-1,0) or no mask (-1,-1)");
+  if (d->dtype == SDPA_DTYPE_FP8_E4M3)
+    return sdpa::set_error(SDPA_ERR_UNSUPPORTED, "context-parallel emulation takes fp16, bf16 or fp32");
   p.cp = cp;
-  p.len = d->seqlen_q / (2 * cp);
+  p.thd = thd;
+  p.len = thd ? (d->seqlen_q + 2 * cp - 1) / (2 * cp) : d->seqlen_q / (2 * cp);
   p.esize = d->dtype == SDPA_DTYPE_F32 ? 4 : 2;
   p.chunk = *d;
   p.chunk.seqlen_q = p.chunk.seqlen_k = p.len;
@@ -73,9 +95,37 @@ int plan(const sdpa_desc_t* d, int cp, const int32_t* hop_order, Plan& p) {
     seen[v] = 1;
     p.order[h] = v;
   }
-  p.part_x = int64_t(d->batch) * d->heads_q * p.len * d->head_dim * p.esize;
-  p.part_l = int64_t(d->batch) * d->heads_q * p.len * 4;
+  if (thd) {
+    p.part_x = d->total_q * d->heads_q * d->head_dim * p.esize;
+    p.part_l = d->total_q * d->heads_q * 4;
+    p.views = round_up(int64_t(2 * cp) * 2 * (d->batch + 1) * 4, 256);
+    size_t fw = 0, bw = 0;
+    int rc;
+    if ((rc = sdpa_fwd_workspace_size(&p.chunk, &fw)) || (rc = sdpa_bwd_workspace_size(&p.chunk, &bw))) return rc;
+    p.attn_bytes = fw > bw ? fw : bw;
+    p.attn_off = p.views + 3 * (round_up(p.part_x, 256) + round_up(p.part_l, 256));
+  } else {
+    p.part_x = int64_t(d->batch) * d->heads_q * p.len * d->head_dim * p.esize;
+    p.part_l = int64_t(d->batch) * d->heads_q * p.len * 4;
+  }
   return SDPA_OK;
+}
+
+// THD: chunk c's view arrays in the workspace (row starts, then the prefix of lengths)
+const int32_t* view_starts(const Plan& p, void* ws, int c) {
+  return static_cast<const int32_t*>(ws) + int64_t(c) * 2 * (p.chunk.batch + 1);
+}
+const int32_t* view_prefix(const Plan& p, void* ws, int c) {
+  return view_starts(p, ws, c) + (p.chunk.batch + 1);
+}
+// The descriptor of pair (q chunk i, kv chunk c) for THD
+sdpa_desc_t thd_pair(const Plan& p, void* ws, int i, int c) {
+  sdpa_desc_t cd = p.chunk;
+  cd.cu_seqlens_q = view_prefix(p, ws, i);
+  cd.cu_seqlens_q_padded = view_starts(p, ws, i);
+  cd.cu_seqlens_k = view_prefix(p, ws, c);
+  cd.cu_seqlens_k_padded = view_starts(p, ws, c);
+  return cd;
 }
 
 bool causal_of(const sdpa_desc_t* d) { return d->window_right == 0; }
@@ -135,6 +185,10 @@ int sdpa_cp_workspace_size(const sdpa_desc_t* desc, int cp, size_t* bytes) {
   int rc = plan(desc, cp, nullptr, p);
   if (rc) return rc;
   if (!bytes) return sdpa::set_error(SDPA_ERR_NULL, "bytes is NULL");
+  if (p.thd) {
+    *bytes = size_t(p.attn_off) + p.attn_bytes;
+    return sdpa::clear_error();
+  }
   size_t bw = 0;
   if ((rc = sdpa_bwd_workspace_size(&p.chunk, &bw))) return rc;
   const int64_t fold = 3 * (round_up(p.part_x, 256) + round_up(p.part_l, 256));
@@ -148,22 +202,39 @@ int sdpa_cp_fwd(const sdpa_desc_t* desc, int cp, const int32_t* hop_order, const
   Plan p;
   int rc = plan(desc, cp, hop_order, p);
   if (rc) return rc;
-  if ((rc = sdpa_fwd_validate(desc, q, k, v, o, lse, 0))) return rc;
+  if ((rc = sdpa_fwd_validate(desc, q, k, v, o, lse, SIZE_MAX))) return rc;
   if (!lse || !lse->data) return sdpa::set_error(SDPA_ERR_NULL, "context-parallel forward needs the LSE output");
   size_t need = 0;
   if ((rc = sdpa_cp_workspace_size(desc, cp, &need))) return rc;
   if (!workspace || workspace_bytes < need) return sdpa::set_error(SDPA_ERR_WORKSPACE, "workspace missing or too small");
 
-  // workspace: partial (x, lse) and two running results, used in turn
+  // workspace: (THD: the chunk views, then) partial (x, lse) and two running results, used
+  // in turn (THD: full-size packed buffers, then the attention calls' own workspace)
   char* ws = static_cast<char*>(workspace);
   const int64_t xs = round_up(p.part_x, 256), ls = round_up(p.part_l, 256);
   sdpa_tensor_t bx[3];
   sdpa_rowstat_t bl[3];
   for (int i = 0; i < 3; ++i) {
-    bx[i] = dense(ws + i * (xs + ls), p.chunk);
-    bl[i] = dense_stat(ws + i * (xs + ls) + xs, p.chunk);
+    char* b = ws + p.views + i * (xs + ls);
+    if (p.thd) {
+      const int64_t h = desc->heads_q, d = desc->head_dim;
+      bx[i] = sdpa_tensor_t{b, {h * d, d, 1, 0}};
+      bl[i] = sdpa_rowstat_t{reinterpret_cast<float*>(b + xs), {desc->total_q, 1, 0}};
+    } else {
+      bx[i] = dense(b, p.chunk);
+      bl[i] = dense_stat(b + xs, p.chunk);
+    }
   }
-  sdpa_merge_desc_t md{desc->layout, desc->dtype, desc->batch, p.len, desc->heads_q, desc->head_dim, 0};
+  void* attn_ws = p.thd ? ws + p.attn_off : nullptr;
+  const size_t attn_bytes = p.thd ? p.attn_bytes : 0;
+  if (p.thd) {
+    if (hipError_t e = sdpa::launch_cp_chunks(desc->cu_seqlens_q, desc->cu_seqlens_q_padded, desc->batch,
+                                              desc->total_q, cp, reinterpret_cast<int32_t*>(ws),
+                                              static_cast<hipStream_t>(stream)))
+      return sdpa::set_error(SDPA_ERR_HIP, hipGetErrorString(e));
+  }
+  sdpa_merge_desc_t md{desc->layout, desc->dtype, desc->batch, p.len, desc->heads_q, desc->head_dim,
+                       p.thd ? desc->total_q : 0, nullptr, nullptr};
   const bool causal = causal_of(desc);
   const int L = p.len, es = p.esize;
   for (int r = 0; r < cp; ++r) {
@@ -181,24 +252,30 @@ int sdpa_cp_fwd(const sdpa_desc_t* desc, int cp, const int32_t* hop_order, const
           if (pair_window(causal, i, c, wl, wr)) kvs.push_back(c);
         }
       }
-      const sdpa_tensor_t qc = chunk_of(*q, desc->layout, i, L, es);
-      const sdpa_tensor_t oc = chunk_of(*o, desc->layout, i, L, es);
-      const sdpa_rowstat_t lc = chunk_of(*lse, i, L);
+      // dense: chunk views; THD: the whole tensors, rows picked by the chunk views
+      const sdpa_tensor_t qc = p.thd ? *q : chunk_of(*q, desc->layout, i, L, es);
+      const sdpa_tensor_t oc = p.thd ? *o : chunk_of(*o, desc->layout, i, L, es);
+      const sdpa_rowstat_t lc = p.thd ? *lse : chunk_of(*lse, i, L);
+      if (p.thd) {
+        md.cu_seqlens = view_prefix(p, ws, i);
+        md.cu_seqlens_padded = view_starts(p, ws, i);
+      }
       int run = -1;  // which buffer holds the running result
       for (size_t n = 0; n < kvs.size(); ++n) {
         const int c = kvs[n];
-        sdpa_desc_t cd = p.chunk;
+        sdpa_desc_t cd = p.thd ? thd_pair(p, ws, i, c) : p.chunk;
         pair_window(causal, i, c, cd.window_left, cd.window_right);
-        const sdpa_tensor_t kc = chunk_of(*k, desc->layout, c, L, es), vc = chunk_of(*v, desc->layout, c, L, es);
+        const sdpa_tensor_t kc = p.thd ? *k : chunk_of(*k, desc->layout, c, L, es);
+        const sdpa_tensor_t vc = p.thd ? *v : chunk_of(*v, desc->layout, c, L, es);
         const bool last = n + 1 == kvs.size();
         if (n == 0) {  // first partial: straight into the running buffer (or the output)
           const sdpa_tensor_t& ox = last ? oc : bx[1];
           const sdpa_rowstat_t& ol = last ? lc : bl[1];
-          if ((rc = sdpa_fwd(&cd, &qc, &kc, &vc, &ox, &ol, nullptr, 0, stream))) return rc;
+          if ((rc = sdpa_fwd(&cd, &qc, &kc, &vc, &ox, &ol, attn_ws, attn_bytes, stream))) return rc;
           run = 1;
           continue;
         }
-        if ((rc = sdpa_fwd(&cd, &qc, &kc, &vc, &bx[0], &bl[0], nullptr, 0, stream))) return rc;
+        if ((rc = sdpa_fwd(&cd, &qc, &kc, &vc, &bx[0], &bl[0], attn_ws, attn_bytes, stream))) return rc;
         const int nxt = run == 1 ? 2 : 1;
         const sdpa_tensor_t& ox = last ? oc : bx[nxt];
         const sdpa_rowstat_t& ol = last ? lc : bl[nxt];
@@ -226,7 +303,21 @@ int sdpa_cp_bwd(const sdpa_desc_t* desc, int cp, const int32_t* hop_order, const
   const bool causal = causal_of(desc);
   const int L = p.len, es = p.esize;
   const bool has_dlse = dlse && dlse->data;
+  char* ws = static_cast<char*>(workspace);
+  if (p.thd) {
+    if (hipError_t e = sdpa::launch_cp_chunks(desc->cu_seqlens_q, desc->cu_seqlens_q_padded, desc->batch,
+                                              desc->total_q, cp, reinterpret_cast<int32_t*>(ws),
+                                              static_cast<hipStream_t>(stream)))
+      return sdpa::set_error(SDPA_ERR_HIP, hipGetErrorString(e));
+  }
   auto pair = [&](int i, int c, int accumulate) {
+    const sdpa_rowstat_t nodl{nullptr, {0, 0, 0}};
+    if (p.thd) {  // whole tensors, rows picked by the chunk views
+      sdpa_desc_t cd = thd_pair(p, ws, i, c);
+      pair_window(causal, i, c, cd.window_left, cd.window_right);
+      return sdpa_bwd(&cd, q, k, v, o, lse, dout, has_dlse ? dlse : &nodl, dq, dk, dv, accumulate,
+                      ws + p.attn_off, p.attn_bytes, stream);
+    }
     sdpa_desc_t cd = p.chunk;
     pair_window(causal, i, c, cd.window_left, cd.window_right);
     const sdpa_tensor_t qc = chunk_of(*q, desc->layout, i, L, es), oc = chunk_of(*o, desc->layout, i, L, es);
@@ -234,7 +325,7 @@ int sdpa_cp_bwd(const sdpa_desc_t* desc, int cp, const int32_t* hop_order, const
     const sdpa_tensor_t kc = chunk_of(*k, desc->layout, c, L, es), vc = chunk_of(*v, desc->layout, c, L, es);
     const sdpa_tensor_t dkc = chunk_of(*dk, desc->layout, c, L, es), dvc = chunk_of(*dv, desc->layout, c, L, es);
     const sdpa_rowstat_t lc = chunk_of(*lse, i, L);
-    const sdpa_rowstat_t dlc = has_dlse ? chunk_of(*dlse, i, L) : sdpa_rowstat_t{nullptr, {0, 0, 0}};
+    const sdpa_rowstat_t dlc = has_dlse ? chunk_of(*dlse, i, L) : nodl;
     return sdpa_bwd(&cd, &qc, &kc, &vc, &oc, &lc, &gc, &dlc, &dqc, &dkc, &dvc, accumulate, workspace,
                     workspace_bytes, stream);
   };

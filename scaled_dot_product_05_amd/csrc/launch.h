@@ -7,6 +7,10 @@
 namespace sdpa {
 
 hipError_t launch_schedule(const SchedParams& p, hipStream_t stream);
+// Context parallelism over THD: per chunk c of 2 cp, the per-sequence row starts and the
+// prefix of chunk lengths (out: int32 [2 cp][2][batch + 1]: starts, then prefix).
+hipError_t launch_cp_chunks(const int32_t* cu, const int32_t* padded, int32_t batch, int64_t total,
+                            int32_t cp, int32_t* out, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, DType dtype, hipStream_t stream);
 // FP8 (E4M3) q, k, v with per-tensor descales, bf16 O
 hipError_t launch_fwd8(const FwdParams& p, hipStream_t stream);

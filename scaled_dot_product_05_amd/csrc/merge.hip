@@ -28,12 +28,31 @@ struct RowPos {
   int64_t b, h, s;
 };
 
+// Row r of the launch: (batch, head, row).  THD with a sequence map enumerates the packed
+// rows of the listed sequences (t = 0 .. cu[nseq] - 1) and places each at its sequence's
+// row start; s = -1 marks a launch row past the last sequence.
 __device__ __forceinline__ RowPos row_pos(const MergeParams& p, int64_t r) {
   RowPos q;
   if (p.thd) {
     q.b = 0;
     q.h = r / p.seqlen;
     q.s = r % p.seqlen;
+    if (p.cu) {
+      const int32_t t = int32_t(q.s), total = p.seqlen;
+      auto at = [&](const int32_t* a, int i) { return min(max(a[i], 0), total); };
+      if (t >= at(p.cu, p.nseq)) {
+        q.s = -1;
+        return q;
+      }
+      int lo = 0, hi = p.nseq;  // the sequence b with cu[b] <= t < cu[b + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (at(p.cu, mid) <= t) lo = mid;
+        else hi = mid;
+      }
+      const int64_t row = int64_t(at(p.pad ? p.pad : p.cu, lo)) + (t - at(p.cu, lo));
+      q.s = row < total ? row : -1;
+    }
   } else {
     q.s = r % p.seqlen;
     int64_t bh = r / p.seqlen;
@@ -96,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void merge_fwd_kernel(MergeParams p) {
   if (r >= p.rows) return;
   const int c = (tid % M::TPR) * M::VPT;
   const RowPos q = row_pos(p, r);
+  if (q.s < 0) return;
   float alpha, beta, lse;
   weights(*srow(p.la, q), *srow(p.lb, q), alpha, beta, lse);
   float a[M::VPT], b[M::VPT], x[M::VPT];
@@ -112,9 +132,9 @@ __global__ __launch_bounds__(kThreads) void merge_bwd_kernel(MergeParams p) {
   using M = RowMap<ES, D>;
   const int tid = threadIdx.x;
   const int64_t r = int64_t(blockIdx.x) * M::RPB + tid / M::TPR;
-  const bool live = r < p.rows;  // every lane takes part in the row reduction below
   const int c = (tid % M::TPR) * M::VPT;
-  const RowPos q = row_pos(p, live ? r : 0);
+  const RowPos q = row_pos(p, r < p.rows ? r : 0);
+  const bool live = r < p.rows && q.s >= 0;  // every lane takes part in the row reduction below
   float alpha = 0.f, beta = 0.f, lse, dot = 0.f;
   float a[M::VPT], b[M::VPT], gg[M::VPT], da[M::VPT], dbv[M::VPT];
   if (live) {

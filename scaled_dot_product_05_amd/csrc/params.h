@@ -97,6 +97,9 @@ struct BwdParams {
 struct MergeParams {
   int64_t rows;          // batch * heads * seqlen, or heads * total
   int32_t batch, seqlen, heads, d, thd;
+  const int32_t* cu;     // THD with a sequence map: cu_seqlens [nseq + 1] (else null)
+  const int32_t* pad;    // ... and sequence row starts (null: cu)
+  int32_t nseq;
   View xa, xb, x, g, dxa, dxb;
   StatView la, lb, l, glse, dla, dlb;
   int32_t aligned;       // all x-like row starts 16-byte aligned

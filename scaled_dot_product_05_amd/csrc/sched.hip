@@ -109,4 +109,39 @@ hipError_t launch_schedule(const SchedParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Context parallelism over THD ("Add support for cuDNN FusedAttention + THD + CP",
+// TransformerEngine issue 885: every sequence of a packed batch is cut into 2 cp chunks).
+// Chunk c of a sequence of length L is rows [floor(c L / 2cp), floor((c+1) L / 2cp)) of it,
+// so a query chunk and the key chunk of the same index cover the same rows.  Thread c
+// writes, for every sequence, the packed row where its chunk c starts (from the padded
+// starts if given) and the prefix sum of the chunk lengths: a padded-THD view of chunk c of
+// every sequence at once.  Entries are clamped to [0, total].
+__global__ __launch_bounds__(128) void cp_chunks_kernel(const int32_t* cu, const int32_t* padded,
+                                                       int32_t batch, int64_t total, int32_t cp,
+                                                       int32_t* out) {
+  const int c = threadIdx.x, n = 2 * cp;
+  if (c >= n) return;
+  int32_t* start = out + int64_t(c) * 2 * (batch + 1);
+  int32_t* pre = start + (batch + 1);
+  auto at = [&](const int32_t* a, int i) { return int64_t(min(max(int64_t(a[i]), int64_t(0)), total)); };
+  int64_t acc = 0;
+  pre[0] = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t len = max(at(cu, b + 1) - at(cu, b), int64_t(0));
+    const int64_t lo = int64_t(c) * len / n, hi = int64_t(c + 1) * len / n;
+    start[b] = int32_t(min(at(padded ? padded : cu, b) + lo, total));
+    acc += hi - lo;
+    pre[b + 1] = int32_t(min(acc, total));
+  }
+  start[batch] = int32_t(total);
+}
+
+hipError_t launch_cp_chunks(const int32_t* cu, const int32_t* padded, int32_t batch, int64_t total,
+                            int32_t cp, int32_t* out, hipStream_t st) {
+  prof_begin(st, "cp_chunks");
+  hipLaunchKernelGGL(cp_chunks_kernel, dim3(1), dim3(128), 0, st, cu, padded, batch, total, cp, out);
+  prof_end(st);
+  return hipGetLastError();
+}
+
 }  // namespace sdpa

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.exported_symbols())
-    assert S.sdpa_version() == 4
+    assert S.sdpa_version() == 5
 
 
 def status_of(fn, *args):
@@ -196,11 +196,16 @@ def test_cp_validation_on_host():
     pw = S.Problem(q, q, "bshd", 0.125, (128, 0))
     with pytest.raises(S.SdpaError):
         S.sdpa_cp_workspace_size(pw.desc, 2)
-    # THD is not supported by the emulation
+    # THD: self-attention with q and k sharing cu_seqlens; any sequence lengths
     cu = torch.tensor([0, 96, 192], dtype=torch.int32)
     pt = S.Problem(q[0], q[0], "thd", 0.125, (-1, 0), cu_seqlens_q=cu, max_seqlen_q=96)
-    with pytest.raises(S.SdpaError):
-        S.sdpa_cp_workspace_size(pt.desc, 2)
+    assert S.sdpa_cp_workspace_size(pt.desc, 5) > 0
+    cu2 = torch.tensor([0, 96, 192], dtype=torch.int32)
+    px = S.Problem(q[0], q[0], "thd", 0.125, (-1, 0), cu_seqlens_q=cu, cu_seqlens_k=cu2,
+                   max_seqlen_q=96)
+    with pytest.raises(S.SdpaError) as e:
+        S.sdpa_cp_workspace_size(px.desc, 2)
+    assert e.value.name == "ERR_UNSUPPORTED"
     # hop_order must be a permutation
     o = torch.empty_like(q)
     lse = torch.empty(2, 4, 192)
