@@ -109,7 +109,7 @@ typedef struct sdpa_rowstat {
  * cu_seqlens_q_padded / cu_seqlens_k_padded  THD only, optional (NULL: sequences packed
  *             back to back): DEVICE int32[batch+1], the packed row where each sequence starts
  *             ("Add support for cuDNN FusedAttention + THD + CP", TransformerEngine issue
- *             885: THD tensors with padding tokens between sequences).  Sequence b occupies
+ *             885: THD tensors with unused rows between packed sequences).  Sequence b occupies
  *             rows [padded[b], padded[b] + (cu_seqlens[b+1] - cu_seqlens[b])); the rows after
  *             it up to padded[b+1] are padding: never read as keys and never written (O, LSE,
  *             dQ, dK and dV of padding rows keep their contents; dLSE/Delta of them are not

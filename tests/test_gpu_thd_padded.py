@@ -1,5 +1,5 @@
 """Padded THD ("Add support for cuDNN FusedAttention + THD + CP", TransformerEngine issue
-885: cu_seqlens_padded, padding tokens between sequences).  The padding rows of q, k, v, dO
+885: cu_seqlens_padded, unused rows between packed sequences).  The padding rows of q, k, v, dO
 hold NaN: if any kernel read them as keys or queries the results would show it.  Outputs
 start as a sentinel, and padding rows must keep it.  Valid rows are checked against the fp64
 oracle and must equal, bit for bit, the same sequences packed without padding."""
