@@ -727,6 +727,208 @@ __global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) 
 }
 
 // ----------------------------------------------------------------------------------------
+// Short query sequences, 16-bit inputs.  With only a few dozen queries per (sequence, head)
+// a 128-row workgroup leaves most of its waves without rows, and the call is bound by the
+// HBM bytes in flight rather than by the matrix cores.  Here each wave is a work unit of its
+// own: 32 query rows of one (sequence, q head), over 32-key tiles, with a private LDS area
+// of two 32-row tiles (Q, then K tiles; V tiles, then the O tile).  Every global access is
+// row-contiguous: lane chunk P = 64 u + lane of a tile is row P / CPR, 16-byte column
+// P % CPR.  Rows then go from LDS into the MFMA operand layouts (K rows as the A operand of
+// S^T = K Q^T, Q rows as its B operand, V through the transposed reads of O^T += V^T P^T),
+// and the O tile returns through LDS to leave as whole rows.  There is no workgroup barrier:
+// the four waves of a block run unrelated items, and the LDS accesses of one wave take
+// effect in issue order.  The next tile's K rows load into registers while the current tile
+// is computed, its V rows once the current P V products are issued.  The softmax takes the exact running max of every tile (VALU time is
+// not what bounds this kernel), so P <= 1.
+// ----------------------------------------------------------------------------------------
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, D >= 128 ? 2 : kFwdShortMinB) void fwd16w_kernel(FwdParams p) {
+  constexpr int BN = 32;
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int NC = D / 16;          // contraction chunks of Q K^T
+  constexpr int NDB = D / 32;         // 32-column blocks of O
+  constexpr int NU = BN * CPR / 64;   // 16-byte chunks per lane per 32-row tile
+  constexpr int TB = BN * D * 2;      // bytes of one 32-row tile
+  static_assert(NU >= 1 && BN * CPR % 64 == 0, "tile split");
+  __shared__ __align__(16) char smem_[kWaves * 2 * TB];
+
+  const Shape& s = p.s;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  lds_t* const ra = (lds_t*)smem_ + wave * 2 * TB;  // Q, then K tiles
+  lds_t* const rb = ra + TB;                        // V tiles, then the O tile
+
+  // item = (q tile, sequence, q head), (sequence, head) fastest
+  const int64_t bh = int64_t(s.batch) * s.hq;
+  const int64_t item = int64_t(blockIdx.x) * kWaves + wave;
+  const int64_t nt = (s.sq + BN - 1) / BN;
+  if (item >= bh * nt) return;
+  const int b = int((item % bh) / s.hq), h = int(item % s.hq);
+  const int q0 = int(item / bh) * BN;
+  const Seq g = seq_of(s, b);
+  if (q0 >= g.sq) return;
+  const int qend = min(q0 + BN, g.sq);
+  const int hk = h / s.group;
+
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint16_t* ob = static_cast<uint16_t*>(p.o.ptr) + b * p.o.sb + h * p.o.sh + g.qrow0 * p.o.ss;
+
+  int j0, j1;
+  key_range(s, g, q0, qend, j0, j1);
+  const int kt0 = j0 / BN;
+  const int kt1 = j1 > j0 ? (j1 + BN - 1) / BN : kt0;
+  // key tiles [wf0, wf1) that every row of the wave sees in full (no mask needed)
+  int wf0, wf1;
+  {
+    const int64_t lo_full = int64_t(qend - 1) + g.off + s.lo_rel;
+    const int64_t hi_full = min(int64_t(q0) + g.off + s.hi_rel, int64_t(g.sk) - 1);
+    const int64_t a = lo_full <= 0 ? 0 : (lo_full + BN - 1) / BN;
+    const int64_t e = hi_full < 0 ? 0 : (hi_full + 1) / BN;
+    wf0 = int(clamp64(a, 0, int64_t(1) << 30));
+    wf1 = int(clamp64(e, wf0, int64_t(1) << 30));
+  }
+
+  // LDS byte offset of 16-byte column c of tile row r: K-like tiles (read 16 rows per
+  // cycle, one column) and V tiles (transposed reads of 4 rows)
+  auto at_k = [](int r, int c) { return (r * CPR + (c ^ swk<CPR>(r))) * 16; };
+  auto at_v = [](int r, int c) { return (r * CPR + (c ^ swv<CPR>(r))) * 16; };
+  typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 kr[NU], vr[NU];
+  auto load_rows = [&](const uint16_t* base, int64_t ss, int row0, int nrows, uint4(&r)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int P = 64 * u + lane, row = row0 + P / CPR;
+      r[u] = row < nrows ? *reinterpret_cast<const uint4*>(base + row * ss + (P % CPR) * 8) : z4;
+    }
+  };
+  auto put = [&](lds_t* dst, bool vt, const uint4(&r)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int P = 64 * u + lane;
+      const int o = vt ? at_v(P / CPR, P % CPR) : at_k(P / CPR, P % CPR);
+      *(lds_u4*)(dst + o) = __builtin_bit_cast(u32x4_t, r[u]);
+    }
+  };
+  int ka[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) ka[cc] = at_k(l32, 2 * cc + hf);
+  int va[NDB];
+  {
+    const int gg = lane >> 4, cr = (lane >> 2) & 3, a = lane & 3;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      va[db] = ((4 * (gg >> 1) + cr) * CPR + ((4 * db + 2 * (gg & 1) + (a >> 1)) ^ swv<CPR>(cr))) * 16 +
+               (a & 1) * 8;
+  }
+
+  const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
+  const uint32_t qsign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
+  uint4 qf[NC];
+  load_rows(qb, p.q.ss, q0, g.sq, kr);
+  if (kt0 < kt1) {
+    load_rows(vb, p.v.ss, kt0 * BN, g.sk, vr);
+  }
+  put(ra, false, kr);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    const uint4 t = lds_read16(ra + ka[cc]);
+    qf[cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
+  }
+  if (kt0 < kt1) load_rows(kb, p.k.ss, kt0 * BN, g.sk, kr);
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+  float m_run = kNegInf, l_run = 0.f;
+  const int qi = q0 + l32;
+  const int hi_eff = qi < g.sq ? min(s.hi_rel, g.sk - 1 - qi - g.off) : s.lo_rel - 1;
+
+  for (int t = kt0; t < kt1; ++t) {
+    if (t > kt0) {
+      load_rows(kb, p.k.ss, t * BN, g.sk, kr);
+      load_rows(vb, p.v.ss, t * BN, g.sk, vr);
+    }
+    // the previous tile's LDS reads were issued before these writes (in-order LDS)
+    asm volatile("" ::: "memory");
+    put(ra, false, kr);
+    put(rb, true, vr);
+    asm volatile("" ::: "memory");
+    f32x16_t st = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) st = mfma16<BF>(lds_read16(ra + ka[cc]), qf[cc], st);
+
+    if (t < wf0 || t >= wf1) {
+      const int base_rel = t * BN - qi - g.off + 4 * hf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rel = base_rel + 8 * (r >> 2) + (r & 3);
+        st[r] = (rel >= s.lo_rel && rel <= hi_eff) ? st[r] : kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx == kNegInf ? kNegInf : mx * c);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    uint4 pf[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(__builtin_fmaf(st[8 * cc + i], c, -m_use));
+      l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      pf[cc] = make_uint4(pack2<BF>(e[0], e[1]), pack2<BF>(e[2], e[3]), pack2<BF>(e[4], e[5]),
+                          pack2<BF>(e[6], e[7]));
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_t* base = rb + 16 * cc * CPR * 16 + va[db];
+        const uint2 lo = read_tr16(base), hi = read_tr16(base + 8 * CPR * 16);
+        acc[db] = mfma16<BF>(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[cc], acc[db]);
+      }
+  }
+
+  // O tile: lane (row l32, d = 32 db + 8 gq + 4 hf .. +3) into LDS, then whole rows out
+  const float lt = sum_halves(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const uint32_t lo = pack2<BF>(acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv);
+      const uint32_t hi = pack2<BF>(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv);
+      typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+      *(__attribute__((address_space(3))) u32x2_t*)(rb + at_k(l32, 4 * db + gq) + 8 * hf) = u32x2_t{lo, hi};
+    }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int P = 64 * u + lane, row = q0 + P / CPR;
+    const uint4 x = lds_read16(rb + at_k(P / CPR, P % CPR));
+    if (row < g.sq) *reinterpret_cast<uint4*>(ob + row * p.o.ss + (P % CPR) * 8) = x;
+  }
+  if (hf == 0 && qi < g.sq && p.lse.ptr) {
+    float* lp = p.lse.ptr + b * p.lse.sb + h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss;
+    *lp = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // fp32 inputs.  Nothing is rounded below fp32 (PyTorch issue 135161 traces its large
 // gradient errors to a tensor-core shortcut inside an "fp32" kernel), and the scores are
 // formed in fp64: fp32 inputs widen exactly, v_mfma_f64_16x16x4 accumulates q.k in fp64,
@@ -980,8 +1182,28 @@ static bool fwd_pipelined(const FwdParams& p) {
 
 bool fwd_block_mask_ok(const FwdParams& p, DType dt) { return dt == DType::F32 || fwd_pipelined(p); }
 
+// Sequences of at most kFwdShortRows queries: one work unit per wave (fwd16w_kernel), which
+// reads rows with 16-byte vector loads, so every row start must be 16-byte aligned.
+static bool fwd_short(const FwdParams& p) {
+  constexpr int need = kAlQ | kAlK | kAlV | kAlO;
+  return kFwdShortRows > 0 && p.s.sq <= kFwdShortRows && !p.s.bm.bits && (p.aligned & need) == need;
+}
+
+template <bool BF, int D>
+static hipError_t go_short(const FwdParams& p, hipStream_t st) {
+  const int64_t items = int64_t(p.s.batch) * p.s.hq * ((p.s.sq + 31) / 32);
+  const int64_t blocks = (items + kWaves - 1) / kWaves;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  prof_begin(st, "attn_fwd_short");
+  hipLaunchKernelGGL((fwd16w_kernel<BF, D>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  prof_end(st);
+  return hipGetLastError();
+}
+
 template <bool BF, int D, int BN, int MINB>
 static hipError_t go16(const FwdParams& p, hipStream_t st) {
+  if (fwd_short(p)) return go_short<BF, D>(p, st);
   constexpr int BM = 32 * kWaves;
   static_assert(BM == kFwdBM16, "host and kernel tile rows differ");
   const int64_t blocks = fwd_grid(p, BM);

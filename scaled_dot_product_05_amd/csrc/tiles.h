@@ -47,6 +47,16 @@ constexpr int kFwdStagesD128 = SDPA_FWD_NS_D128;  // K/V LDS slots, head_dim 128
 #endif
 constexpr bool kFwdWideD64 = SDPA_FWD_WIDE_D64;      // 64 query rows per wave, head_dim 64
 constexpr int kFwdWideMinBlocks = SDPA_FWD_WIDE_MIN;  // ... when the grid has this many blocks
+#ifndef SDPA_FWD_SHORT_ROWS
+#define SDPA_FWD_SHORT_ROWS 32
+#endif
+// queries per sequence up to which every wave of the 16-bit forward is a work unit of its own
+// (32 query rows of one (sequence, q head)); 0 turns that kernel off
+constexpr int kFwdShortRows = SDPA_FWD_SHORT_ROWS;
+#ifndef SDPA_FWD_SHORT_MINB
+#define SDPA_FWD_SHORT_MINB 3
+#endif
+constexpr int kFwdShortMinB = SDPA_FWD_SHORT_MINB;  // its workgroups per CU, head_dim <= 64
 
 // backward dQ: one workgroup owns kBwdQ16 (16-bit) or kBwdQ32 (fp32) query rows; keys stream
 // in kBwdQInner tiles (16-bit) or 32-key tiles (fp32)
