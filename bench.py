@@ -31,7 +31,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {  # which source file holds each kernel (for the traffic-staleness check)
     "attn_fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_pre": "bwd.hip",
     "bwd_main": "bwd.hip",
-    "merge_fwd": "merge.hip", "merge_bwd": "merge.hip",
+    "merge_fwd": "merge.hip", "merge_bwd": "merge.hip", "attn_fwd_short": "fwd.hip",
 }
 
 
@@ -85,9 +85,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra measurements")
-    ap.add_argument("--workload", choices=("c2", "target"), default="c2",
+    ap.add_argument("--workload", choices=("c2", "target") + tuple(HBM_WORKLOADS), default="c2",
                     help="c2: causal bf16 fwd+bwd B4 S1024 H8 D64 (default); target: causal bf16 "
-                         "forward only, B8 S4096 H8 D64 (for profiling the forward kernel)")
+                         "forward only, B8 S4096 H8 D64 (for profiling the forward kernel); "
+                         "short / merge: the HBM-bound short-sequence forward and merge kernels "
+                         "(for profiling them; the line reports GB/s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
     args = ap.parse_args()
@@ -105,6 +107,8 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     S.lib()
+    if args.workload in HBM_WORKLOADS:
+        return hbm_main(args, torch, S, synth, dev)
 
     # ---------------- the step: causal bf16 fwd + bwd, B4 S1024 H8 D64 ----------------
     fwd_only = args.workload == "target"
@@ -214,6 +218,86 @@ def main() -> int:
     return 0
 
 
+HBM_WORKLOADS = {
+    "short": ("short-sequence forward, bf16, B4096 S32 H16 D64, no mask, BSHD contiguous, "
+              "scale 1/8, N(0,1) inputs"),
+    "merge": ("LSE merge forward + backward, fp32, x [4,8192,16,128] BSHD, lse [4,16,8192], "
+              "N(0,1) inputs"),
+}
+
+
+def hbm_main(args, torch, S, synth, dev) -> int:
+    """The HBM-bound kernels on their own: one step is a short-sequence forward, or a merge
+    forward plus its backward.  Algorithmic bytes per launch: every input read once and
+    every output written once."""
+    if args.workload == "short":
+        b, s, h, d = 4096, 32, 16, 64
+        w = synth.dense(0, 6, "bf16", "bshd", b, s, s, h, h, d, 0.125, name="short")
+        q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+        o = torch.empty_like(q)
+        lse = torch.empty(b, h, s, dtype=torch.float32, device=dev)
+
+        def step():
+            S.forward(q, k, v, "bshd", 0.125, (-1, -1), out=o, lse=lse)
+        alg = {"attn_fwd_short": 4 * q.numel() * 2 + lse.numel() * 4}
+        cfg = {"batch": b, "seq_len": s, "heads": h, "head_dim": d, "mask": "none"}
+    else:
+        b, s, h, d = 4, 8192, 16, 128
+        g = torch.Generator().manual_seed(7)
+        xa, xb, gx = (torch.randn(b, s, h, d, generator=g).to(dev) for _ in range(3))
+        la, lb, gl = (torch.randn(b, h, s, generator=g).to(dev) for _ in range(3))
+        x, l = torch.empty_like(xa), torch.empty_like(la)
+        rows = b * s * h
+
+        def step():
+            S.merge(xa, la, xb, lb, "bshd", out=x, lse=l)
+            S.merge_backward(xa, la, xb, lb, gx, gl, "bshd")
+        alg = {"merge_fwd": rows * (3 * d * 4 + 3 * 4), "merge_bwd": rows * (5 * d * 4 + 5 * 4)}
+        cfg = {"batch": b, "seq_len": s, "heads": h, "head_dim": d}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with Timer(torch) as tm:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = max(wall_ms, tm.ms() / args.steps)
+    S.sdpa_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(False)
+    kern = S.sdpa_profile_read()
+    kernels = {}
+    for name, (n, tot) in kern.items():
+        avg = tot / n
+        rec = {"launches": n, "avg_ms": avg}
+        if name in alg:
+            ach = alg[name] / (avg * 1e-3) / 1e9
+            rec.update({"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes_per_launch": alg[name],
+                        "traffic": traffic_for(name, args.workload)})
+        kernels[name] = rec
+        log(f"{name}: {avg * 1e3:.2f} us/launch", rec.get("achieved", ""), "GB/s")
+    dom = max((n for n in kern if n in alg), key=lambda n: kern[n][1])
+    roof = {k: kernels[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof.update({"kernel": dom, "avg_launch_ms": round(kernels[dom]["avg_ms"], 6)})
+    total = sum(alg.values())
+    print(json.dumps({
+        "metric": "HBM GB/s of the " + ("short-sequence forward" if args.workload == "short"
+                                        else "LSE merge kernels"),
+        "value": round(total / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if args.workload == "short" else "f32", "data": "synthetic",
+        "config": {"workload": HBM_WORKLOADS[args.workload], **cfg},
+        "roofline": roof, "kernels": kernels}), flush=True)
+    return 0
+
+
 def copy_calibration() -> int:
     """A plain 1 GiB device-to-device copy, 5 times: its HBM counters read 1 GiB per
     dispatch in each direction, which gives the scale of FETCH_SIZE / WRITE_SIZE."""
@@ -302,7 +386,7 @@ def extra(torch, S, synth, dev):
 
     # short sequences (HBM bound): non-causal bf16 D64, B*H*S = 2^21
     ss = []
-    for s in (32, 128, 512):
+    for s in (16, 32, 64, 128, 512):
         b = (1 << 21) // (16 * s)
         q, k, v = (torch.randn(b, s, 16, 64, device=dev, dtype=torch.bfloat16) for _ in range(3))
         o = torch.empty_like(q)

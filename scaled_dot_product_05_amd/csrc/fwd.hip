@@ -795,13 +795,14 @@ __global__ __launch_bounds__(kThreads, D >= 128 ? 2 : kFwdShortMinB) void fwd16w
   auto at_k = [](int r, int c) { return (r * CPR + (c ^ swk<CPR>(r))) * 16; };
   auto at_v = [](int r, int c) { return (r * CPR + (c ^ swv<CPR>(r))) * 16; };
   typedef __attribute__((address_space(3))) u32x4_t lds_u4;
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
   uint4 kr[NU], vr[NU];
   auto load_rows = [&](const uint16_t* base, int64_t ss, int row0, int nrows, uint4(&r)[NU]) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int P = 64 * u + lane, row = row0 + P / CPR;
-      r[u] = row < nrows ? *reinterpret_cast<const uint4*>(base + row * ss + (P % CPR) * 8) : z4;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (row < nrows) x = *reinterpret_cast<const uint4*>(base + row * ss + (P % CPR) * 8);
+      r[u] = x;
     }
   };
   auto put = [&](lds_t* dst, bool vt, const uint4(&r)[NU]) {
