@@ -1390,6 +1390,234 @@ __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_fused16p_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// Short sequences, 16-bit inputs, head_dim <= 64: at most 32 queries and 32 keys per
+// sequence.  The tiled kernels then run on mostly empty 64-row tiles and the call is bound
+// by HBM bytes in flight.  Here each wave is a work unit of its own: the keys of one
+// (sequence, kv head), and in turn every q head of its group.  Delta_i = dO_i . O_i - dLSE_i
+// is formed in the wave (no pre-pass).  Every global access is row-contiguous (lane chunk
+// 64 u + lane of a 32-row tile is row (64 u + lane) / CPR, 16-byte column
+// (64 u + lane) % CPR); rows pass through private LDS tiles into the MFMA layouts:
+//   S = Q K^T and dP = dO V^T with the key as the MFMA column (lane = key, registers =
+//     queries 8 (r / 4) + 4 half + r % 4);
+//   dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T from transposed LDS reads whose
+//     query order matches the registers of P and dS;
+//   dQ^T = K^T dS^T, with dS staged in LDS as [key][query] and read back transposed.
+// dK, dV accumulate in registers over the group; dQ leaves after each head.  LDS accesses of
+// one wave take effect in issue order, so there is no barrier.
+// ----------------------------------------------------------------------------------------
+template <bool BF, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd16w_kernel(BwdParams p) {
+  constexpr int BN = 32;
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int NC = D / 16;         // contraction chunks over d
+  constexpr int NDB = D / 32;        // 32-column blocks of d
+  constexpr int NU = BN * CPR / 64;  // 16-byte chunks per lane per 32-row tile
+  constexpr int TB = BN * D * 2;     // bytes of a 32-row tile
+  constexpr int WB = 4 * TB + 2 * BN * 4;
+  static_assert(NU >= 1 && D <= 64, "tile split");
+  __shared__ __align__(16) char smem_[kWaves * WB];
+
+  const Shape& s = p.s;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  lds_t* const tq = (lds_t*)smem_ + wave * WB;  // Q tile, then the dQ tile
+  lds_t* const tk = tq + TB;                    // K tile, then the dK tile
+  lds_t* const tdo = tk + TB;                   // dO tile, then the dV tile
+  lds_t* const tvs = tdo + TB;                  // V tile, then dS [key][query]
+  lds_t* const tst = tvs + TB;                  // LSE log2(e) [32], Delta [32]
+
+  const int64_t item = int64_t(blockIdx.x) * kWaves + wave;
+  if (item >= int64_t(s.batch) * s.hk) return;
+  const int b = int(item / s.hk), hk = int(item % s.hk);
+  const Seq g = seq_of(s, b);
+
+  auto at_v = [](int r, int c) { return (r * CPR + (c ^ swv<CPR>(r))) * 16; };
+  auto at_k = [](int r, int c) { return (r * CPR + (c ^ swk<CPR>(r))) * 16; };
+  typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+  typedef __attribute__((address_space(3))) float lds_f;
+  auto load_rows = [&](const uint16_t* base, int64_t ss, int nrows, uint4(&r)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int P = 64 * u + lane, row = P / CPR;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (row < nrows) x = *reinterpret_cast<const uint4*>(base + row * ss + (P % CPR) * 8);
+      r[u] = x;
+    }
+  };
+  auto put = [&](lds_t* dst, const uint4(&r)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int P = 64 * u + lane;
+      *(lds_u4*)(dst + at_v(P / CPR, P % CPR)) = __builtin_bit_cast(u32x4_t, r[u]);
+    }
+  };
+  // transposed-read addresses: tiles [32 rows][D] (V layout) and dS [32 keys][32 queries]
+  int va[NDB], vs;
+  {
+    const int gg = lane >> 4, cr = (lane >> 2) & 3, a = lane & 3;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      va[db] = ((4 * (gg >> 1) + cr) * CPR + ((4 * db + 2 * (gg & 1) + (a >> 1)) ^ swv<CPR>(cr))) * 16 +
+               (a & 1) * 8;
+    vs = ((4 * (gg >> 1) + cr) * 4 + 2 * (gg & 1) + (a >> 1)) * 16 + (a & 1) * 8;
+  }
+  auto tr = [&](const lds_t* base, int pitch_chunks, int cc) {
+    const lds_t* q = base + 16 * cc * pitch_chunks * 16;
+    const uint2 lo = read_tr16(q), hi = read_tr16(q + 8 * pitch_chunks * 16);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+  // a [32 rows][D] C-layout result (lane = row l32, d = 32 db + 8 gq + 4 hf + 0..3) to rows
+  // of dst, through an LDS tile; scaled, and added to the old values if asked
+  auto store_tile = [&](lds_t* stage, const f32x16_t(&acc)[NDB], float scale, uint16_t* dst, int64_t ss, int nrows) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t v = {pack2<BF>(acc[db][4 * gq] * scale, acc[db][4 * gq + 1] * scale),
+                           pack2<BF>(acc[db][4 * gq + 2] * scale, acc[db][4 * gq + 3] * scale)};
+        *(__attribute__((address_space(3))) u32x2_t*)(stage + at_k(l32, 4 * db + gq) + 8 * hf) = v;
+      }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int P = 64 * u + lane, row = P / CPR;
+      uint4 x = lds_read16(stage + at_k(row, P % CPR));
+      if (row < nrows) {
+        uint4* o = reinterpret_cast<uint4*>(dst + row * ss + (P % CPR) * 8);
+        if (p.accumulate) {
+          const uint4 old = *o;
+          float a[8], c[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            a[e] = to_f32<BF>(uint16_t(elem16(x, e)));
+            c[e] = to_f32<BF>(uint16_t(elem16(old, e)));
+          }
+          x = make_uint4(pack2<BF>(a[0] + c[0], a[1] + c[1]), pack2<BF>(a[2] + c[2], a[3] + c[3]),
+                         pack2<BF>(a[4] + c[4], a[5] + c[5]), pack2<BF>(a[6] + c[6], a[7] + c[7]));
+        }
+        *o = x;
+      }
+    }
+  };
+
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k.ptr) + b * p.k.sb + hk * p.k.sh + g.krow0 * p.k.ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v.ptr) + b * p.v.sb + hk * p.v.sh + g.krow0 * p.v.ss;
+  uint4 ra[NU], rb[NU], rc[NU];
+  load_rows(kb, p.k.ss, g.sk, ra);
+  load_rows(vb, p.v.ss, g.sk, rb);
+  put(tk, ra);
+  put(tvs, rb);
+  asm volatile("" ::: "memory");
+  uint4 kf[NC], vf[NC];  // lane = key l32, d chunk 16 cc + 8 hf
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    kf[cc] = lds_read16(tk + at_v(l32, 2 * cc + hf));
+    vf[cc] = lds_read16(tvs + at_v(l32, 2 * cc + hf));
+  }
+  f32x16_t dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero16();
+  const int j = l32;  // this lane's key
+
+  for (int h = hk * s.group; h < (hk + 1) * s.group; ++h) {
+    const uint16_t* qb = static_cast<const uint16_t*>(p.q.ptr) + b * p.q.sb + h * p.q.sh + g.qrow0 * p.q.ss;
+    const uint16_t* gb = static_cast<const uint16_t*>(p.dout.ptr) + b * p.dout.sb + h * p.dout.sh + g.qrow0 * p.dout.ss;
+    const uint16_t* ob = static_cast<const uint16_t*>(p.o.ptr) + b * p.o.sb + h * p.o.sh + g.qrow0 * p.o.ss;
+    load_rows(qb, p.q.ss, g.sq, ra);
+    load_rows(gb, p.dout.ss, g.sq, rb);
+    load_rows(ob, p.o.ss, g.sq, rc);
+    // Delta of each row: 8-element partial dots, summed over the CPR lanes of the row
+    float dl = 0.f, l2 = __builtin_inff();
+    if (hf == 0 && l32 < g.sq) {
+      const int64_t so = b * p.lse.sb + h * p.lse.sh + (g.qrow0 + l32) * p.lse.ss;
+      const float l = p.lse.ptr[so];
+      l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+      if (p.dlse.ptr) dl = p.dlse.ptr[b * p.dlse.sb + h * p.dlse.sh + (g.qrow0 + l32) * p.dlse.ss];
+    }
+    asm volatile("" ::: "memory");
+    if (hf == 0) ((lds_f*)tst)[l32] = l2;
+    // the dS reads of the previous head were issued before these writes (in-order LDS)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dot += to_f32<BF>(uint16_t(elem16(rb[u], e))) * to_f32<BF>(uint16_t(elem16(rc[u], e)));
+#pragma unroll
+      for (int off = CPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+      const int P = 64 * u + lane;
+      if (P % CPR == 0) ((lds_f*)tst)[BN + P / CPR] = dot;
+    }
+    put(tq, ra);
+    put(tdo, rb);
+    asm volatile("" ::: "memory");
+    if (hf == 0) ((lds_f*)tst)[BN + l32] -= dl;
+    asm volatile("" ::: "memory");
+
+    f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      st = mfma16<BF>(lds_read16(tq + at_v(l32, 2 * cc + hf)), kf[cc], st);
+      dp = mfma16<BF>(lds_read16(tdo + at_v(l32, 2 * cc + hf)), vf[cc], dp);
+    }
+    float pr[16], ds[16];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int i0 = 8 * gi + 4 * hf;
+      const f32x4_t L = *(const __attribute__((address_space(3))) f32x4_t*)(tst + 4 * i0);
+      const f32x4_t Dl = *(const __attribute__((address_space(3))) f32x4_t*)(tst + 4 * (BN + i0));
+      const float lv[4] = {L[0], L[1], L[2], L[3]}, dv4[4] = {Dl[0], Dl[1], Dl[2], Dl[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * gi + e, i = i0 + e, rel = j - i - g.off;
+        const bool vis = i < g.sq && j < g.sk && rel >= s.lo_rel && rel <= s.hi_rel;
+        pr[r] = vis ? fast_exp2(__builtin_fmaf(st[r], s.scale_log2, -lv[e])) : 0.f;
+        ds[r] = pr[r] * (dp[r] - dv4[e]);
+      }
+    }
+    uint4 pf[2], sf[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      pf[cc] = make_uint4(pack2<BF>(pr[8 * cc], pr[8 * cc + 1]), pack2<BF>(pr[8 * cc + 2], pr[8 * cc + 3]),
+                          pack2<BF>(pr[8 * cc + 4], pr[8 * cc + 5]), pack2<BF>(pr[8 * cc + 6], pr[8 * cc + 7]));
+      sf[cc] = make_uint4(pack2<BF>(ds[8 * cc], ds[8 * cc + 1]), pack2<BF>(ds[8 * cc + 2], ds[8 * cc + 3]),
+                          pack2<BF>(ds[8 * cc + 4], ds[8 * cc + 5]), pack2<BF>(ds[8 * cc + 6], ds[8 * cc + 7]));
+    }
+    // dS as [key][query]: registers 4 gi .. 4 gi + 3 are queries 8 gi + 4 hf + 0..3
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+      const uint4 w = sf[gi >> 1];
+      const u32x2_t v = (gi & 1) ? u32x2_t{w.z, w.w} : u32x2_t{w.x, w.y};
+      *(__attribute__((address_space(3))) u32x2_t*)(tvs + j * 64 + (8 * gi + 4 * hf) * 2) = v;
+    }
+    asm volatile("" ::: "memory");
+    f32x16_t dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const uint4 sT = tr(tvs + vs, 4, cc);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = mfma16<BF>(tr(tdo + va[db], CPR, cc), pf[cc], dv[db]);
+        dk[db] = mfma16<BF>(tr(tq + va[db], CPR, cc), sf[cc], dk[db]);
+        dq[db] = mfma16<BF>(tr(tk + va[db], CPR, cc), sT, dq[db]);
+      }
+    }
+    uint16_t* dqb = static_cast<uint16_t*>(p.dq.ptr) + b * p.dq.sb + h * p.dq.sh + g.qrow0 * p.dq.ss;
+    store_tile(tq, dq, s.scale, dqb, p.dq.ss, g.sq);
+  }
+  uint16_t* dkb = static_cast<uint16_t*>(p.dk.ptr) + b * p.dk.sb + hk * p.dk.sh + g.krow0 * p.dk.ss;
+  uint16_t* dvb = static_cast<uint16_t*>(p.dv.ptr) + b * p.dv.sb + hk * p.dv.sh + g.krow0 * p.dv.ss;
+  store_tile(tdo, dv, 1.f, dvb, p.dv.ss, g.sk);
+  store_tile(tk, dk, s.scale, dkb, p.dk.ss, g.sk);
+}
+
+// ----------------------------------------------------------------------------------------
 // launches
 // ----------------------------------------------------------------------------------------
 template <class K>
@@ -1480,8 +1708,32 @@ bool bwd_block_mask_ok(const BwdParams& p, DType dt) {
   return kv && q && (p.s.bm.nh == 1 || int64_t(p.s.group) * p.s.bm.nqb <= kMaskMaxList);
 }
 
+// Sequences of at most kBwdShortRows queries and keys, head_dim <= 64: one work unit per wave
+// (bwd16w_kernel, no pre-pass); its row-contiguous 16-byte accesses need every row start of
+// q, k, v, o, dO, dq, dk, dv 16-byte aligned.
+static bool bwd_short(const BwdParams& p, DType dt) {
+  constexpr int need = kAlQ | kAlK | kAlV | kAlO | kAlDO | kAlDQ | kAlDK | kAlDV;
+  return kBwdShortRows > 0 && dt != DType::F32 && p.s.d <= 64 && p.s.sq <= kBwdShortRows &&
+         p.s.sk <= kBwdShortRows && !p.s.bm.bits && (p.aligned & need) == need;
+}
+
+template <bool BF>
+static hipError_t go_bwd_short(const BwdParams& p, hipStream_t st) {
+  const int64_t blocks = (int64_t(p.s.batch) * p.s.hk + kWaves - 1) / kWaves;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  prof_begin(st, "bwd_short");
+  if (p.s.d == 32)
+    hipLaunchKernelGGL((bwd16w_kernel<BF, 32>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd16w_kernel<BF, 64>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
+  prof_end(st);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
   const Shape& s = p.s;
+  if (bwd_short(p, dt)) return dt == DType::BF16 ? go_bwd_short<true>(p, st) : go_bwd_short<false>(p, st);
   hipError_t e = dt == DType::F32 ? pre<4, false>(p, st)
                                    : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
   if (e != hipSuccess) return e;

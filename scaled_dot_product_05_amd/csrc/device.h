@@ -248,6 +248,21 @@ __device__ __forceinline__ uint32_t bm_dword(const BlockMaskP& m, int64_t plane,
   return reinterpret_cast<const uint32_t*>(m.bits + (plane * sq + i) * int64_t(m.words))[dw];
 }
 
+// 16-byte chunk swizzles of row-major LDS tiles of CPR chunks per row (chunk c of row r sits
+// at slot c ^ sw(r)).
+// LDS serves 256 bytes (64 banks) per cycle; a 16-byte read covers 16 lanes per cycle and
+// an 8-byte read 32 lanes.  K reads take one chunk of 16 consecutive rows, so those rows
+// must fall on 16 distinct 16-byte bank slots; transposed V reads take 4 consecutive rows
+// x 64 bytes per 32 lanes, so those 4 rows must fall on distinct 64-byte bank quarters.
+template <int CPR>
+__device__ __forceinline__ int swk(int r) {
+  return CPR >= 16 ? (r & 15) : CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+template <int CPR>
+__device__ __forceinline__ int swv(int r) {
+  return CPR >= 16 ? 4 * (r & 3) : CPR == 8 ? 2 * (r & 3) : 0;
+}
+
 struct Seq {
   int64_t qrow0, krow0;
   int32_t sq, sk, off;

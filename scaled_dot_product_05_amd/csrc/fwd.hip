@@ -331,18 +331,6 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16_kernel(FwdParams p) {
 // products of tile t follow.  Loads for K(t+2) and V(t+1) are issued at the top of step t
 // and waited for at its end, one barrier per tile.
 // ----------------------------------------------------------------------------------------
-// LDS serves 256 bytes (64 banks) per cycle; a 16-byte read covers 16 lanes per cycle and
-// an 8-byte read 32 lanes.  K reads take one chunk of 16 consecutive rows, so those rows
-// must fall on 16 distinct 16-byte bank slots; transposed V reads take 4 consecutive rows
-// x 64 bytes per 32 lanes, so those 4 rows must fall on distinct 64-byte bank quarters.
-template <int CPR>
-__device__ __forceinline__ int swk(int r) {
-  return CPR >= 16 ? (r & 15) : CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-}
-template <int CPR>
-__device__ __forceinline__ int swv(int r) {
-  return CPR >= 16 ? 4 * (r & 3) : CPR == 8 ? 2 * (r & 3) : 0;
-}
 
 // QB = query blocks of 32 per wave: with QB = 2 every K or V operand read from LDS feeds two
 // products, halving LDS reads per flop, and each K/V tile serves 256 query rows.

@@ -69,6 +69,13 @@ constexpr int kBwdK16 = 64;
 constexpr int kBwdK32 = 128;
 constexpr int kBwdKInner = 64;
 
+// backward: queries and keys per sequence up to which every wave is a work unit of its own
+// (head_dim <= 64); 0 turns that kernel off
+#ifndef SDPA_BWD_SHORT_ROWS
+#define SDPA_BWD_SHORT_ROWS 32
+#endif
+constexpr int kBwdShortRows = SDPA_BWD_SHORT_ROWS;
+
 // THD scheduler buckets (costs above the last bucket share it)
 constexpr int kSchedBuckets = 4096;
 

@@ -1,10 +1,11 @@
-"""GPU parity of the short-sequence forward against the fp64 oracle.
+"""GPU parity of the short-sequence kernels against the fp64 oracle.
 
 Calls whose sequences hold at most 32 queries run a forward in which every wave is a work
-unit of its own (32 query rows of one (sequence, q head)); these cases cover it across
-dtypes, head dims, key lengths with ragged tails, windows, both diagonal alignments, GQA,
-packed views, THD (plain and padded), fully masked rows and a large batch checked on
-sampled (batch, head) pairs.  The backward that follows runs on the O and LSE it wrote.
+unit of its own (32 query rows of one (sequence, q head)); with at most 32 keys as well and
+head_dim <= 64 the backward does the same per (sequence, kv head).  These cases cover both
+across dtypes, head dims, key lengths with ragged tails, windows, both diagonal alignments,
+GQA, dLSE, accumulation, packed views, THD (plain and padded), fully masked rows and a
+large batch checked on sampled (batch, head) pairs; each asserts which kernels ran.
 """
 import numpy as np
 import pytest
@@ -43,9 +44,13 @@ def run_case(w, backward=True):
     o_ref, lse_ref = oracle_forward(w)
     check_forward(gpu_bhsd(o, w), synth.f64(lse), o_ref, lse_ref, w.dtype, "fwd")
     if backward:
-        dq, dk, dv = gpu_backward(w, q, k, v, o, lse, w.dout.to(DEV), None, cq, ck)
-        torch.cuda.synchronize()
-        check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], oracle_backward(w), w.dtype, "bwd")
+        dl = w.dlse.to(DEV) if w.dlse is not None else None
+        names = kernels_of(lambda: res.update(g=gpu_backward(w, q, k, v, o, lse, w.dout.to(DEV),
+                                                             dl, cq, ck)))
+        short_bwd = w.seqlen_q <= 32 and w.seqlen_k <= 32 and w.head_dim <= 64
+        assert ("bwd_short" in names) == short_bwd, names
+        refs = oracle_backward(w, synth.f64(w.dlse) if dl is not None else None)
+        check_grads([gpu_bhsd(t, w) for t in res["g"]], refs, w.dtype, "bwd")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -135,3 +140,37 @@ def test_large_batch_sampled():
     o_ref, lse_ref = oracle.windowed_forward(qs, ks, vs, w.scale, w.window, 0)
     og = synth.f64(synth.to_bhsd(o[pick].cpu(), "bshd"))
     check_forward(og, synth.f64(lse[pick]), o_ref, lse_ref, "bf16", "sampled fwd")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_backward_groups_dlse_bottom_right(dtype):
+    w = synth.dense(39, 980, dtype, "bshd", 3, 20, 29, 8, 2, 64, 0.2, (-1, 0), 1,
+                    with_grad=True, with_dlse=True, name="short_bwd_gqa")
+    run_case(w)
+
+
+def test_backward_accumulates():
+    w = synth.dense(40, 990, "bf16", "sbhd", 2, 32, 32, 4, 4, 64, 0.125, (7, 0),
+                    with_grad=True, name="short_bwd_acc")
+    q, k, v = to_dev(w)
+    o, lse = gpu_forward(w, q, k, v)
+    g = w.dout.to(DEV)
+    dq, dk, dv = gpu_backward(w, q, k, v, o, lse, g)
+    names = kernels_of(lambda: gpu_backward(w, q, k, v, o, lse, g, dq=dq, dk=dk, dv=dv,
+                                            accumulate=True))
+    assert "bwd_short" in names, names
+    refs = [2 * r for r in oracle_backward(w)]
+    check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], refs, "bf16", "bwd accumulated twice")
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_backward_thd_short_sequences(d):
+    w = synth.thd(41, 1000 + d, "bf16", [1, 0, 32, 17, 5, 31], 8, 2, d, d ** -0.5, (-1, 0),
+                  with_grad=True, with_dlse=True, name="short_bwd_thd")
+    run_case(w)
+
+
+def test_backward_thd_cross_lengths():
+    w = synth.thd(42, 1010, "f16", [3, 32, 9, 0], 4, 4, 64, 0.3, (-1, 0), with_grad=True,
+                  lengths_k=[30, 7, 32, 5], diag_align=1, name="short_bwd_thd_cross")
+    run_case(w)
