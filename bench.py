@@ -32,6 +32,7 @@ KERNEL_SOURCES = {  # which source file holds each kernel (for the traffic-stale
     "attn_fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_pre": "bwd.hip",
     "bwd_main": "bwd.hip",
     "merge_fwd": "merge.hip", "merge_bwd": "merge.hip", "attn_fwd_short": "fwd.hip",
+    "bwd_short": "bwd.hip",
 }
 
 
@@ -219,27 +220,32 @@ def main() -> int:
 
 
 HBM_WORKLOADS = {
-    "short": ("short-sequence forward, bf16, B4096 S32 H16 D64, no mask, BSHD contiguous, "
-              "scale 1/8, N(0,1) inputs"),
+    "short": ("short-sequence forward + backward, bf16, B4096 S32 H16 D64, no mask, BSHD "
+              "contiguous, scale 1/8, N(0,1) inputs"),
     "merge": ("LSE merge forward + backward, fp32, x [4,8192,16,128] BSHD, lse [4,16,8192], "
               "N(0,1) inputs"),
 }
 
 
 def hbm_main(args, torch, S, synth, dev) -> int:
-    """The HBM-bound kernels on their own: one step is a short-sequence forward, or a merge
-    forward plus its backward.  Algorithmic bytes per launch: every input read once and
-    every output written once."""
+    """The HBM-bound kernels on their own: one step is a short-sequence forward plus its
+    backward, or a merge forward plus its backward.  Algorithmic bytes per launch: every
+    input read once and every output written once."""
     if args.workload == "short":
         b, s, h, d = 4096, 32, 16, 64
-        w = synth.dense(0, 6, "bf16", "bshd", b, s, s, h, h, d, 0.125, name="short")
-        q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+        w = synth.dense(0, 6, "bf16", "bshd", b, s, s, h, h, d, 0.125, with_grad=True,
+                        name="short")
+        q, k, v, g = (t.to(dev) for t in (w.q, w.k, w.v, w.dout))
         o = torch.empty_like(q)
         lse = torch.empty(b, h, s, dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
         def step():
             S.forward(q, k, v, "bshd", 0.125, (-1, -1), out=o, lse=lse)
-        alg = {"attn_fwd_short": 4 * q.numel() * 2 + lse.numel() * 4}
+            S.backward(q, k, v, o, lse, g, "bshd", 0.125, (-1, -1), dq=dq, dk=dk, dv=dv)
+        tb = q.numel() * 2
+        alg = {"attn_fwd_short": 4 * tb + lse.numel() * 4,  # q, k, v in; o, lse out
+               "bwd_short": 8 * tb + lse.numel() * 4}      # q, k, v, o, dO, lse in; dq, dk, dv out
         cfg = {"batch": b, "seq_len": s, "heads": h, "head_dim": d, "mask": "none"}
     else:
         b, s, h, d = 4, 8192, 16, 128
@@ -287,8 +293,8 @@ def hbm_main(args, torch, S, synth, dev) -> int:
     roof.update({"kernel": dom, "avg_launch_ms": round(kernels[dom]["avg_ms"], 6)})
     total = sum(alg.values())
     print(json.dumps({
-        "metric": "HBM GB/s of the " + ("short-sequence forward" if args.workload == "short"
-                                        else "LSE merge kernels"),
+        "metric": "HBM GB/s of the " + ("short-sequence forward and backward"
+                                        if args.workload == "short" else "LSE merge kernels"),
         "value": round(total / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -393,9 +399,15 @@ def extra(torch, S, synth, dev):
         lse = torch.empty(b, 16, s, device=dev)
         ms = time_calls(torch, lambda: S.forward(q, k, v, "bshd", 0.125, out=o, lse=lse))
         nbytes = 4 * q.numel() * 2 + lse.numel() * 4
+        g = torch.randn_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        msb = time_calls(torch, lambda: S.backward(q, k, v, o, lse, g, "bshd", 0.125, dq=dq,
+                                                   dk=dk, dv=dv))
+        bbytes = 8 * q.numel() * 2 + lse.numel() * 4
         ss.append({"S": s, "B": b, "H": 16, "ms": round(ms, 4),
-                   "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
-        del q, k, v, o, lse
+                   "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bwd_ms": round(msb, 4),
+                   "bwd_GB/s": round(bbytes / (msb * 1e-3) / 1e9, 1)})
+        del q, k, v, o, lse, g, dq, dk, dv
     res["short_seq_fwd_bf16"] = ss
     try:
         clk = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
