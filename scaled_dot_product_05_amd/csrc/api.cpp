@@ -356,10 +356,23 @@ size_t fwd_ws_bytes(const Shape& s, int32_t dtype) {
 
 struct BwdWs {
   int64_t delta_off, lse2_off, wq_off, cq_off, wk_off, ck_off, total;
+  int64_t split_blocks, cnt_off, part_off;  // split dK/dV (split_blocks = 0: none)
 };
 
 int bwd_q_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdQ32 : kBwdQ16; }
 int bwd_k_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdK32 : kBwdK16; }
+
+// Split dK/dV blocks: GQA groups, 16-bit inputs, head_dim 64 or 128, no block mask, and a
+// block count that fits the kernel's int32 block index.
+bool bwd_split_ok(const Shape& s, int32_t dtype) {
+  if (kBwdSplit == 0 || s.group < 2 || dtype == SDPA_DTYPE_F32 || dtype == SDPA_DTYPE_FP8_E4M3 ||
+      (s.d != 64 && s.d != 128) || s.bm.bits)
+    return false;
+  const int64_t tk = kBwdK16;
+  const int64_t nk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk
+                           : ((s.sk + tk - 1) / tk) * int64_t(s.batch) * s.hk;
+  return nk * 2 < (int64_t(1) << 30);
+}
 
 BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
   BwdWs w{};
@@ -376,6 +389,17 @@ BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
     off = round_up(off + thd_items(s.total_k, s.batch, bwd_k_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
     w.ck_off = off;
     off += 256;
+  }
+  // GQA on the fused 16-bit backward: every dK/dV block runs as two halves whose fp32
+  // partial sums (2 halves x 64 keys x D x {dK, dV}) meet in the workspace
+  if (bwd_split_ok(s, dtype)) {
+    const int64_t tk = kBwdK16;
+    w.split_blocks = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk
+                           : ((s.sk + tk - 1) / tk) * int64_t(s.batch) * s.hk;
+    w.cnt_off = off;
+    off = round_up(off + w.split_blocks * 4, 256);
+    w.part_off = off;
+    off = round_up(off + w.split_blocks * 2 * 64 * int64_t(s.d) * 2 * 4, 256);
   }
   w.total = off;
   return w;
@@ -783,6 +807,13 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   p.lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
   p.ws_rows = a.s.thd ? int64_t(a.s.hq) * a.s.total_q : int64_t(a.s.batch) * a.s.hq * a.s.sq;
   p.accumulate = accumulate;
+  p.nsplit = 1;
+  if (w.split_blocks > 0) {
+    p.nsplit = 2;
+    p.split_blocks = int32_t(w.split_blocks);
+    p.split_cnt = reinterpret_cast<int32_t*>(ws + w.cnt_off);
+    p.split_part = reinterpret_cast<float*>(ws + w.part_off);
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (a.s.thd) {

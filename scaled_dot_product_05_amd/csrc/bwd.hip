@@ -52,6 +52,11 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
     h = bh % s.hq;
     b = bh / s.hq;
   }
+  if (p.nsplit > 1) {
+    // counters of the split dK/dV blocks of the launch that follows on this stream
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + tid; i < p.split_blocks; i += int64_t(gridDim.x) * kThreads)
+      p.split_cnt[i] = 0;
+  }
   const int c = (tid % TPR) * VPT;
   float dot = 0.f;
   if (live) {
@@ -1074,7 +1079,8 @@ struct DkdvP {
 };
 
 template <bool BF, int D, int W, bool BSM>
-__device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid) {
+__device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid, int split = 0,
+                                             int nsplit = 1) {
   constexpr int BK = 32 * W, BQ = DkdvP<D, W>::BQ, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DkdvP<D, W>::TB, NDMA = BQ * CPR / NT;
   constexpr int NC = D / 16, NDB = D / 32, NPC = BQ / 16;
@@ -1132,8 +1138,20 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     }
     __syncthreads();
   }
+  // a split block takes the first or the second half of the items
+  int ib = 0;
+  if (nsplit == 2) {
+    const int n1 = (n + 1) / 2;
+    if (split == 0) {
+      n = n1;
+    } else {
+      ib = n1;
+      n -= n1;
+    }
+  }
   // item it -> q head (within the group), q tile, and whether its block needs the bits
   auto item = [&](int it, int& gi, int& qt, bool& part) {
+    it += ib;
     if constexpr (BSM) {
       int e, r;
       if (s.bm.nh == 1) {
@@ -1347,6 +1365,35 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
+  if (nsplit == 2) {
+    // Each half stores its fp32 sums (in register order, one 256-byte row per register),
+    // makes them visible at device scope and counts itself in; the half that arrives second
+    // adds the other half's sums (a + b: the same value whichever half it is) and writes.
+    constexpr int PR = 2 * NDB * 16 * 64;  // floats per wave and half
+    float* mine = p.split_part + (int64_t(bid) * 2 * W + split * W + wave) * PR;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mine[(db * 16 + r) * 64 + lane] = adk[db][r];
+        mine[((NDB + db) * 16 + r) * 64 + lane] = adv[db][r];
+      }
+    __threadfence();
+    __shared__ int32_t arrived;
+    __syncthreads();
+    if (tid == 0) arrived = __hip_atomic_fetch_add(p.split_cnt + bid, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != 1) return;
+    __threadfence();
+    const float* other = p.split_part + (int64_t(bid) * 2 * W + (split ^ 1) * W + wave) * PR;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        adk[db][r] += other[(db * 16 + r) * 64 + lane];
+        adv[db][r] += other[((NDB + db) * 16 + r) * 64 + lane];
+      }
+  }
   if (kj < g.sk) {
     uint16_t* krow = dkb + kj * p.dk.ss;
     uint16_t* vrow = dvb + kj * p.dv.ss;
@@ -1383,10 +1430,19 @@ template <bool BF, int D, int W, bool BSM>
 __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_fused16p_kernel(BwdParams p, int nk) {
   constexpr int L = DqP<D, W>::LDS > DkdvP<D, W>::LDS ? DqP<D, W>::LDS : DkdvP<D, W>::LDS;
   __shared__ __align__(16) char smem_[L];
-  if (int(blockIdx.x) < nk)
-    dkdv16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, blockIdx.x);
+  const int bid = blockIdx.x;
+  if (!BSM && p.nsplit == 2) {
+    // GQA: block 2 i + h is half h of dK/dV block i
+    if (bid < 2 * nk)
+      dkdv16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, bid >> 1, bid & 1, 2);
+    else
+      dq16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, bid - 2 * nk);
+    return;
+  }
+  if (bid < nk)
+    dkdv16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, bid);
   else
-    dq16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, int(blockIdx.x) - nk);
+    dq16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, bid - nk);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1646,7 +1702,8 @@ static hipError_t pre(const BwdParams& p, hipStream_t st) {
   int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
   auto launch = [&](auto kernel, int d) {
     int rpb = kThreads / (d / (16 / ES));
-    return go(kernel, "bwd_pre", (rows + rpb - 1) / rpb, st, p);
+    const int64_t blocks = (rows + rpb - 1) / rpb;
+    return go(kernel, "bwd_pre", p.nsplit > 1 && blocks < 1 ? 1 : blocks, st, p);  // it zeroes the split counters
   };
   if (s.d == 32) return launch(bwd_pre_kernel<ES, BF, 32>, 32);
   if (s.d == 64) return launch(bwd_pre_kernel<ES, BF, 64>, 64);
@@ -1661,11 +1718,16 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
     const bool q = pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
     if (kv && q) {
       if (bk + bq <= 0) return hipSuccess;
+      const bool split = !p.s.bm.bits && p.nsplit == 2 && bk == p.split_blocks;
+      BwdParams ps = p;
+      ps.nsplit = split ? 2 : 1;
+      const int64_t grid = bk * ps.nsplit + bq;
+      if (grid > 0x7fffffff) return hipErrorInvalidValue;
       prof_begin(st, "bwd_main");
       if (p.s.bm.bits)
-        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, true>), dim3(unsigned(bk + bq)), dim3(128), 0, st, p, int(bk));
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, true>), dim3(unsigned(grid)), dim3(128), 0, st, ps, int(bk));
       else
-        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, false>), dim3(unsigned(bk + bq)), dim3(128), 0, st, p, int(bk));
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, false>), dim3(unsigned(grid)), dim3(128), 0, st, ps, int(bk));
       prof_end(st);
       return hipGetLastError();
     }

@@ -92,6 +92,12 @@ struct BwdParams {
   const int32_t* count_k;
   int32_t aligned;
   int32_t accumulate;
+  // dK/dV blocks split in two over their (q head, q tile) items (GQA): fp32 partial sums of
+  // each half and a per-block counter (zeroed by the pre-pass); nsplit = 1: no split
+  int32_t nsplit;
+  int32_t split_blocks;  // dK/dV blocks (counters)
+  int32_t* split_cnt;
+  float* split_part;
 };
 
 struct MergeParams {

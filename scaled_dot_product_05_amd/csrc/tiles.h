@@ -76,6 +76,12 @@ constexpr int kBwdKInner = 64;
 #endif
 constexpr int kBwdShortRows = SDPA_BWD_SHORT_ROWS;
 
+// backward: GQA dK/dV blocks of the fused 16-bit kernel run as two halves (0: off)
+#ifndef SDPA_BWD_SPLIT
+#define SDPA_BWD_SPLIT 1
+#endif
+constexpr int kBwdSplit = SDPA_BWD_SPLIT;
+
 // THD scheduler buckets (costs above the last bucket share it)
 constexpr int kSchedBuckets = 4096;
 

@@ -119,3 +119,26 @@ def test_unaligned_rows_take_the_element_path():
     check_forward(gpu_bhsd(o, w), synth.f64(lse), o_ref, lse_ref, "bf16", "unaligned fwd")
     dq, dk, dv = gpu_backward(w, q, k, v, o, lse, w.dout.to(DEV))
     check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], oracle_backward(w), "bf16", "unaligned bwd")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gqa_backward_split_is_deterministic(d):
+    # GQA dK/dV blocks run as two halves that meet in the workspace; two calls must give the
+    # same bits, and both must match the oracle
+    w = synth.dense(21, 900 + d, "bf16", "bshd", 2, 300, 300, 8, 2, d, d ** -0.5, (-1, 0),
+                    with_grad=True, name="gqa_split")
+    q, k, v = to_dev(w)
+    o, lse = gpu_forward(w, q, k, v)
+    g = w.dout.to(DEV)
+    first = gpu_backward(w, q, k, v, o, lse, g)
+    second = gpu_backward(w, q, k, v, o, lse, g)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
+    check_grads([gpu_bhsd(t, w) for t in first], oracle_backward(w), "bf16", "gqa split bwd")
+
+
+def test_gqa_backward_split_thd():
+    w = synth.thd(22, 910, "f16", [300, 0, 65, 1, 200], 8, 2, 128, 0.1, (-1, 0), with_grad=True,
+                  with_dlse=True)
+    run_case(w, dlse=True)

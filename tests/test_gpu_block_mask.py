@@ -134,7 +134,9 @@ def test_empty_rows_and_block_rows():
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
 def test_all_ones_mask_reproduces_the_unmasked_kernels_bitwise(dtype, d):
-    w = synth.dense(27, 440, dtype, "bshd", 2, 640, 640, 4, 2, d, d ** -0.5, (-1, 0),
+    # one kv head per q head: with GQA the unmasked backward sums each dK/dV block in two
+    # halves (a different fp32 order), the block-sparse one in a single pass
+    w = synth.dense(27, 440, dtype, "bshd", 2, 640, 640, 4, 4, d, d ** -0.5, (-1, 0),
                     with_grad=True, name="bmones")
     say(f"case all-ones {dtype} D={d}")
     q, k, v = to_dev(w)
