@@ -241,7 +241,9 @@ int sdpa_fwd_fp8(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_ten
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward workspace size in bytes: fp32 Delta_i = dO_i . O_i - dLSE_i and fp32
- * LSE_i * log2(e) for every q row, plus the THD work lists.  Host only. */
+ * LSE_i * log2(e) for every q row, plus the THD work lists, plus under GQA (16-bit inputs,
+ * head_dim 64 or 128, no block mask) the fp32 partial dK/dV sums of the two halves of every
+ * 64-key block (1 KiB x head_dim per block) and one counter per block.  Host only. */
 int sdpa_bwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes);
 
 /* Host-only dry run of sdpa_bwd's validation. */
@@ -254,8 +256,10 @@ int sdpa_bwd_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdp
 /* Backward from the saved LSE (PyTorch issue 135161: gradients through O and through the
  * returned LSE).  Reads q, k, v, o, lse (from sdpa_fwd), dout and optionally dlse
  * (dlse == NULL or dlse->data == NULL means dL/dLSE = 0).  Writes dq (q's shape), dk and dv
- * (k's shape; summed over the q heads of each group).  No atomics: every output element
- * has one writer.  accumulate = 0 overwrites, 1 adds to the existing contents (to sum the
+ * (k's shape; summed over the q heads of each group).  No atomic accumulation: every output
+ * element has one writer (under GQA the second of a block's two halves to finish, found with
+ * one atomic counter per block, adds the first half's partial sums in fp32; the result does
+ * not depend on which half finishes first).  accumulate = 0 overwrites, 1 adds to the existing contents (to sum the
  * gradients of several partial attentions into one buffer). */
 int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
              const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
