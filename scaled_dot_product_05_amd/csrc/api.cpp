@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 
 #include <hip/hip_runtime_api.h>
@@ -362,16 +363,34 @@ struct BwdWs {
 int bwd_q_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdQ32 : kBwdQ16; }
 int bwd_k_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdK32 : kBwdK16; }
 
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Split dK/dV blocks: GQA groups, 16-bit inputs, head_dim 64 or 128, no block mask, and a
-// block count that fits the kernel's int32 block index.
+// small grid (at most kBwdSplitPerCU dK/dV plus dQ blocks per CU of the current device),
+// where the longest dK/dV chain (G times the longest dQ chain) sets the time.  On larger
+// grids the extra blocks and the partial sums cost more than the shorter chain saves.
 bool bwd_split_ok(const Shape& s, int32_t dtype) {
   if (kBwdSplit == 0 || s.group < 2 || dtype == SDPA_DTYPE_F32 || dtype == SDPA_DTYPE_FP8_E4M3 ||
       (s.d != 64 && s.d != 128) || s.bm.bits)
     return false;
-  const int64_t tk = kBwdK16;
+  const int64_t tk = kBwdK16, tq = kBwdQ16;
   const int64_t nk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk
                            : ((s.sk + tk - 1) / tk) * int64_t(s.batch) * s.hk;
-  return nk * 2 < (int64_t(1) << 30);
+  const int64_t nq = s.thd ? ((s.total_q + tq - 1) / tq + s.batch) * s.hq
+                           : ((s.sq + tq - 1) / tq) * int64_t(s.batch) * s.hq;
+  return nk + nq <= int64_t(kBwdSplitPerCU) * device_cus() && nk * 2 < (int64_t(1) << 30);
 }
 
 BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {

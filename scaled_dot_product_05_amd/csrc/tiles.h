@@ -81,6 +81,7 @@ constexpr int kBwdShortRows = SDPA_BWD_SHORT_ROWS;
 #define SDPA_BWD_SPLIT 1
 #endif
 constexpr int kBwdSplit = SDPA_BWD_SPLIT;
+constexpr int kBwdSplitPerCU = 8;  // ... when the grid has at most this many blocks per CU
 
 // THD scheduler buckets (costs above the last bucket share it)
 constexpr int kSchedBuckets = 4096;
