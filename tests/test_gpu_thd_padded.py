@@ -30,7 +30,18 @@ def _padded(t, rows, total):
     ("f32", 2, 2, 64, (-1, 0)),
 ])
 def test_padded_thd_matches_oracle_and_packed(dtype, hq, hk, d, window):
-    lengths, gaps = [300, 1, 0, 129, 64], [5, 0, 3, 17, 2]
+    run_padded(dtype, hq, hk, d, window, [300, 1, 0, 129, 64], [5, 0, 3, 17, 2])
+
+
+@pytest.mark.parametrize("hq,hk", [(4, 2), (4, 4)])
+def test_padded_thd_short_sequences(hq, hk):
+    # at most 32 rows per sequence: the short-sequence forward and backward kernels
+    names = run_padded("bf16", hq, hk, 64, (-1, 0), [30, 1, 0, 17, 32], [5, 0, 3, 17, 2])
+    assert {"attn_fwd_short", "bwd_short"} <= names, names
+
+
+def run_padded(dtype, hq, hk, d, window, lengths, gaps):
+    """Returns the names of the kernels the padded calls launched."""
     w = synth.thd(4, 41, dtype, lengths, hq, hk, d, d ** -0.5, window, with_grad=True)
     cu = w.cu_seqlens_q
     pad = np.concatenate([[0], np.cumsum(np.add(lengths, gaps))]).astype(np.int32)
@@ -45,12 +56,16 @@ def test_padded_thd_matches_oracle_and_packed(dtype, hq, hk, d, window):
     tdt = qp.dtype
     o = torch.full_like(qp, SENTINEL)
     lse = torch.full((hq, total), SENTINEL, dtype=torch.float32, device=DEV)
+    dq, dk, dv = (torch.full_like(t, SENTINEL) for t in (qp, kp, vp))
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(True)
     S.forward(qp, kp, vp, "thd", w.scale, window, "top_left", cq, cq, smax, smax, out=o, lse=lse,
               cu_seqlens_q_padded=cp, cu_seqlens_k_padded=cp)
-    dq, dk, dv = (torch.full_like(t, SENTINEL) for t in (qp, kp, vp))
     S.backward(qp, kp, vp, o, lse, gp, "thd", w.scale, window, "top_left", None, cq, cq, smax, smax,
                dq=dq, dk=dk, dv=dv, cu_seqlens_q_padded=cp, cu_seqlens_k_padded=cp)
     torch.cuda.synchronize()
+    S.sdpa_profile_enable(False)
+    names = set(S.sdpa_profile_read())
     # padding rows untouched
     gi = torch.from_numpy(gap).to(DEV)
     for t in (o, dq, dk, dv):
@@ -70,3 +85,4 @@ def test_padded_thd_matches_oracle_and_packed(dtype, hq, hk, d, window):
     assert torch.equal(o[ri], o2) and torch.equal(lse[:, ri], l2)
     for a, b in zip((dq, dk, dv), d2):
         assert torch.equal(a[ri], b)
+    return names
