@@ -1078,9 +1078,8 @@ struct DkdvP {
   static constexpr int LDS = NS * SB;
 };
 
-template <bool BF, int D, int W, bool BSM>
-__device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid, int split = 0,
-                                             int nsplit = 1) {
+template <bool BF, int D, int W, bool BSM, bool SPLIT = false>
+__device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid, int split = 0) {
   constexpr int BK = 32 * W, BQ = DkdvP<D, W>::BQ, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DkdvP<D, W>::TB, NDMA = BQ * CPR / NT;
   constexpr int NC = D / 16, NDB = D / 32, NPC = BQ / 16;
@@ -1140,7 +1139,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
   // a split block takes the first or the second half of the items
   int ib = 0;
-  if (nsplit == 2) {
+  if constexpr (SPLIT) {
     const int n1 = (n + 1) / 2;
     if (split == 0) {
       n = n1;
@@ -1151,7 +1150,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
   // item it -> q head (within the group), q tile, and whether its block needs the bits
   auto item = [&](int it, int& gi, int& qt, bool& part) {
-    it += ib;
+    if constexpr (SPLIT) it += ib;
     if constexpr (BSM) {
       int e, r;
       if (s.bm.nh == 1) {
@@ -1365,7 +1364,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
-  if (nsplit == 2) {
+  if constexpr (SPLIT) {
     // Each half stores its fp32 sums (in register order, one 256-byte row per register),
     // makes them visible at device scope and counts itself in; the half that arrives second
     // adds the other half's sums (a + b: the same value whichever half it is) and writes.
@@ -1426,15 +1425,16 @@ __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dkdv16p_kernel(B
 // dK/dV and dQ in one launch: blocks [0, nk) take key tiles, the rest query tiles.  The two
 // halves are independent, so on small problems they fill the chip together instead of one
 // after the other.
-template <bool BF, int D, int W, bool BSM>
+template <bool BF, int D, int W, bool BSM, bool SPLIT>
 __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_fused16p_kernel(BwdParams p, int nk) {
   constexpr int L = DqP<D, W>::LDS > DkdvP<D, W>::LDS ? DqP<D, W>::LDS : DkdvP<D, W>::LDS;
   __shared__ __align__(16) char smem_[L];
   const int bid = blockIdx.x;
-  if (!BSM && p.nsplit == 2) {
+  if constexpr (SPLIT) {
     // GQA: block 2 i + h is half h of dK/dV block i
+    static_assert(!BSM, "no split under a block mask");
     if (bid < 2 * nk)
-      dkdv16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, bid >> 1, bid & 1, 2);
+      dkdv16p_body<BF, D, W, BSM, true>(p, (lds_t*)smem_, bid >> 1, bid & 1);
     else
       dq16p_body<BF, D, W, BSM>(p, (lds_t*)smem_, bid - 2 * nk);
     return;
@@ -1719,15 +1719,15 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
     if (kv && q) {
       if (bk + bq <= 0) return hipSuccess;
       const bool split = !p.s.bm.bits && p.nsplit == 2 && bk == p.split_blocks;
-      BwdParams ps = p;
-      ps.nsplit = split ? 2 : 1;
-      const int64_t grid = bk * ps.nsplit + bq;
+      const int64_t grid = bk * (split ? 2 : 1) + bq;
       if (grid > 0x7fffffff) return hipErrorInvalidValue;
       prof_begin(st, "bwd_main");
       if (p.s.bm.bits)
-        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, true>), dim3(unsigned(grid)), dim3(128), 0, st, ps, int(bk));
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, true, false>), dim3(unsigned(grid)), dim3(128), 0, st, p, int(bk));
+      else if (split)
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, false, true>), dim3(unsigned(grid)), dim3(128), 0, st, p, int(bk));
       else
-        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, false>), dim3(unsigned(grid)), dim3(128), 0, st, ps, int(bk));
+        hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, false, false>), dim3(unsigned(grid)), dim3(128), 0, st, p, int(bk));
       prof_end(st);
       return hipGetLastError();
     }
