@@ -86,11 +86,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra measurements")
-    ap.add_argument("--workload", choices=("c2", "target") + tuple(HBM_WORKLOADS), default="c2",
+    ap.add_argument("--workload", choices=tuple(MFMA_WORKLOADS) + tuple(HBM_WORKLOADS), default="c2",
                     help="c2: causal bf16 fwd+bwd B4 S1024 H8 D64 (default); target: causal bf16 "
-                         "forward only, B8 S4096 H8 D64 (for profiling the forward kernel); "
-                         "short / merge: the HBM-bound short-sequence forward and merge kernels "
-                         "(for profiling them; the line reports GB/s)")
+                         "forward only, B8 S4096 H8 D64; target_d128: the same forward at H16 "
+                         "D128; target_step: fwd+bwd at B8 S4096 H8 D64 (the last three for "
+                         "profiling the long-sequence kernels); short / merge: the HBM-bound "
+                         "short-sequence forward and merge kernels (for profiling them; the "
+                         "line reports GB/s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
     args = ap.parse_args()
@@ -112,8 +114,10 @@ def main() -> int:
         return hbm_main(args, torch, S, synth, dev)
 
     # ---------------- the step: causal bf16 fwd + bwd, B4 S1024 H8 D64 ----------------
-    fwd_only = args.workload == "target"
-    w = synth.target() if fwd_only else synth.c2()
+    fwd_only = args.workload in ("target", "target_d128")
+    w = {"c2": lambda: synth.c2(), "target": lambda: synth.target(),
+         "target_d128": lambda: synth.target(h=16, d=128),
+         "target_step": lambda: synth.target(with_grad=True)}[args.workload]()
     q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
     g = torch.empty_like(q) if fwd_only else w.dout.to(dev)
     pr = S.Problem(q, k, "bshd", w.scale, w.window)
@@ -196,10 +200,7 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": ("causal self-attention forward, bf16, B8 S4096 H8 D64, BSHD "
-                                "contiguous, scale 1/8, N(0,1) inputs") if fwd_only else
-                               ("causal self-attention fwd+bwd, bf16, B4 S1024 H8 D64, BSHD "
-                                "contiguous, scale 1/8, N(0,1) inputs"),
+        "config": {"workload": MFMA_WORKLOADS[args.workload],
                    "batch": w.batch, "seq_len": w.seqlen_q, "heads": w.heads_q,
                    "head_dim": w.head_dim, "mask": "causal", "flops_per_step": flops_step},
         "frac_of_peak": round(value / PEAK_TFLOPS["bf16"], 5),
@@ -212,12 +213,23 @@ def main() -> int:
     if not args.no_extra:
         out["extra"] = extra(torch, S, synth, dev)
 
-    if not args.no_cpu and not fwd_only:
+    if not args.no_cpu and args.workload == "c2":
         out["cpu_baseline"] = cpu_baseline(w, flops_step)
 
     print(json.dumps(out), flush=True)
     return 0
 
+
+MFMA_WORKLOADS = {
+    "c2": ("causal self-attention fwd+bwd, bf16, B4 S1024 H8 D64, BSHD contiguous, scale 1/8, "
+           "N(0,1) inputs"),
+    "target": ("causal self-attention forward, bf16, B8 S4096 H8 D64, BSHD contiguous, scale 1/8, "
+               "N(0,1) inputs"),
+    "target_d128": ("causal self-attention forward, bf16, B8 S4096 H16 D128, BSHD contiguous, "
+                    "scale 1/sqrt(128), N(0,1) inputs"),
+    "target_step": ("causal self-attention fwd+bwd, bf16, B8 S4096 H8 D64, BSHD contiguous, "
+                    "scale 1/8, N(0,1) inputs"),
+}
 
 HBM_WORKLOADS = {
     "short": ("short-sequence forward + backward, bf16, B4096 S32 H16 D64, no mask, BSHD "
