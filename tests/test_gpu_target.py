@@ -1,14 +1,15 @@
 """The long-sequence causal case at full size (batch 8, 4096 tokens, bf16, BSHD), in the
-launch configuration the benchmark times: the full O and LSE come from the HIP path, and
-sampled rows (tile edges, first and last rows, random rows of several heads) are checked
-against the fp64 oracle one row at a time."""
+launch configuration the benchmark times: the full O and LSE (and dQ, dK, dV) come from the
+HIP path, and sampled rows (tile edges, first and last rows, random rows of several heads)
+are checked against the fp64 oracle one row at a time; sampled dK/dV rows (key rows) are
+checked against the oracle's sums over every query row of the kv head's group."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from gpu_util import DEV, LSE_TOL, O_TOL, gpu_forward, say
+from gpu_util import DEV, G_TOL, LSE_TOL, O_TOL, gpu_backward, gpu_forward, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,3 +40,37 @@ def test_target_causal_sampled_rows(h, hk, d):
         worst_l = max(worst_l, float(np.abs(synth.f64(lse[b, hh, rows]) - rl).max()))
     say(f"  sampled rows: max |O err| {worst_o:.2e}, max |LSE err| {worst_l:.2e}")
     assert worst_o <= O_TOL["bf16"] and worst_l <= LSE_TOL
+
+
+@pytest.mark.parametrize("h,hk,d", [(8, 8, 64), (16, 4, 128)])
+def test_target_backward_sampled(h, hk, d):
+    w = synth.target(seed=4, h=h, hk=hk, d=d, with_grad=True)
+    say(f"case target backward B{w.batch} S{w.seqlen_q} H{h}/{hk} D{d}")
+    q, k, v, g = (t.to(DEV) for t in (w.q, w.k, w.v, w.dout))
+    o, lse = gpu_forward(w, q, k, v)
+    dq, dk, dv = gpu_backward(w, q, k, v, o, lse, g)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    rng = np.random.default_rng(12)
+    group = h // hk
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for b, kh in [(1, 0), (w.batch - 2, hk - 1)]:
+        heads = list(range(kh * group, (kh + 1) * group))
+        kg, vg = synth.f64(w.k[b, :, kh]), synth.f64(w.v[b, :, kh])
+        qh = np.stack([synth.f64(w.q[b, :, hh]) for hh in heads])
+        gh = np.stack([synth.f64(w.dout[b, :, hh]) for hh in heads])
+        rows = _rows(w.seqlen_q, rng)
+        for i, hh in enumerate(heads[:2]):
+            got["dq"].append(synth.f64(dq[b, rows, hh]))
+            ref["dq"].append(oracle.dq_rows(qh[i], kg, vg, gh[i], w.scale, rows, w.window))
+        cols = _rows(w.seqlen_k, rng)
+        rk, rv = oracle.dkdv_cols(qh, kg, vg, gh, w.scale, cols, w.window)
+        got["dk"].append(synth.f64(dk[b, cols, kh]))
+        got["dv"].append(synth.f64(dv[b, cols, kh]))
+        ref["dk"].append(rk)
+        ref["dv"].append(rv)
+    errs = {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= G_TOL["bf16"], f"{n}: {e}"
