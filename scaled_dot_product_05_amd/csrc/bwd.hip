@@ -981,13 +981,19 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
     }
   };
   // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
-  auto grad = [&](int t, bool part, int slot, const f32x16_t& st, const f32x16_t& dp, uint4(&dsf)[NPC]) {
-    float ds[16];
+  // x = s c - LSE log2e and y = dP - Delta of the current tile: the first uses of its S and
+  // dP, taken before the next tile's products overwrite those registers
+  auto consume = [&](const f32x16_t& st, const f32x16_t& dp, float(&x)[16], float(&y)[16]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pr = fast_exp2(__builtin_fmaf(st[r], c, -lse2));
-      ds[r] = pr * (dp[r] - dl);
+      x[r] = __builtin_fmaf(st[r], c, -lse2);
+      y[r] = dp[r] - dl;
     }
+  };
+  auto grad = [&](int t, bool part, int slot, const float(&x)[16], const float(&y)[16], uint4(&dsf)[NPC]) {
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(x[r]) * y[r];
     if (part || t < wf0 || t >= wf1) {
       asm volatile("" ::: "memory");
       const int base_rel = t * BN - qi - g.off + 4 * hf;
@@ -1033,20 +1039,36 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   // Step i: tile t = kt0 + i in K and V slot t % 4.  The products of tile t+1 are issued
   // before tile t's dS, so the matrix cores run while the VALU works; before its barrier a
   // step waits for every load but its own, so tile t+2 has landed.
+  // head_dim <= 64 (two waves per SIMD): one pair of score registers; each step first takes
+  // the current tile's S and dP into their first uses, then issues the next tile's
+  // products into the same registers (their MFMAs run while the VALU exponentiates), so no
+  // register copies carry them over.  head_dim 128 (one wave per SIMD) gains more from the
+  // compiler interleaving the next products with the whole softmax, at the price of the
+  // copies (measured: D64 B8 S4096 backward 568 -> 548 us, D128 B4 S4096 1180 -> 1273 us).
   f32x16_t sa, da, sb, db_;
   if (n > 0) products(0, 0, sa, da);
   for (int i = 0; i < n; ++i) {
     const int ph = i & 3;
     issue_k(tile_at(i + 3), (ph + 3) & 3, i + 3 < n && partial_at(i + 3));
     issue_v(tile_at(i + 3), (ph + 3) & 3);
-    products((ph + 1) & 3, (ph + 1) & 3, sb, db_);  // past the last tile: unused
+    float x[16], y[16];
+    if constexpr (D <= 64) {
+      consume(sa, da, x, y);
+      __builtin_amdgcn_sched_barrier(0);
+      products((ph + 1) & 3, (ph + 1) & 3, sa, da);  // past the last tile: unused
+    } else {
+      products((ph + 1) & 3, (ph + 1) & 3, sb, db_);
+      consume(sa, da, x, y);
+    }
     uint4 dsf[NPC];
-    grad(tile_at(i), partial_at(i), ph, sa, da, dsf);
+    grad(tile_at(i), partial_at(i), ph, x, y, dsf);
     dq_update(ph, dsf);
     vm_wait<2 * NDMA + NB>();
     lds_barrier();
-    sa = sb;
-    da = db_;
+    if constexpr (D > 64) {
+      sa = sb;
+      da = db_;
+    }
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
@@ -1268,15 +1290,11 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       dp = mfma16<BF>(b2, vf[cc], dp);
     }
   };
-  // P, dS and the dV, dK updates of item `it` (slot sl), given its S and dP
-  auto update = [&](int sl, int it, const f32x16_t& st, const f32x16_t& dp) {
+  // x = s c - LSE log2e and y = dP - Delta of item in slot sl: the first uses of its S and
+  // dP, taken before the next item's products overwrite those registers.
+  // lane = key; register r holds query 8(r/4) + 4hf + r%4 of the tile
+  auto consume = [&](int sl, const f32x16_t& st, const f32x16_t& dp, float(&x)[16], float(&y)[16]) {
     const lds_t* base = lds + sl * SB;
-    int gi, qt;
-    bool part;
-    item(it, gi, qt, part);
-    const int qbase = qt * BQ;
-    // lane = key; register r holds query 8(r/4) + 4hf + r%4 of the tile
-    float pr[16], ds[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint4 l4 = lds_read16(base + 2 * TB + (8 * j + 4 * hf) * 4);
@@ -1285,10 +1303,23 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       const float da[4] = {__uint_as_float(d4.x), __uint_as_float(d4.y), __uint_as_float(d4.z), __uint_as_float(d4.w)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 4 * j + e;
-        pr[r] = fast_exp2(__builtin_fmaf(st[r], c, -la[e]));
-        ds[r] = pr[r] * (dp[r] - da[e]);
+        x[4 * j + e] = __builtin_fmaf(st[4 * j + e], c, -la[e]);
+        y[4 * j + e] = dp[4 * j + e] - da[e];
       }
+    }
+  };
+  // P, dS and the dV, dK updates of item `it` (slot sl), given consume's x and y
+  auto update = [&](int sl, int it, const float(&x)[16], const float(&y)[16]) {
+    const lds_t* base = lds + sl * SB;
+    int gi, qt;
+    bool part;
+    item(it, gi, qt, part);
+    const int qbase = qt * BQ;
+    float pr[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = fast_exp2(x[r]);
+      ds[r] = pr[r] * y[r];
     }
     if (part || qt < wq0 || qt >= wq1) {
       asm volatile("" ::: "memory");
@@ -1340,7 +1371,10 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
 
   // Step it reads item it (slot it % 4) and item it+1 (the next S and dP, issued before
   // this item's softmax so the matrix cores run while the VALU works), loads item it+3 and
-  // before its barrier waits for every load but its own, so item it+2 has landed.
+  // before its barrier waits for every load but its own, so item it+2 has landed.  At
+  // head_dim <= 64 one pair of score registers: the current item's S and dP are taken into
+  // their first uses before the next item's products are issued into the same registers
+  // (no copies); head_dim 128 keeps two pairs and lets the compiler interleave (as in dQ).
   f32x16_t sa, da, sb, db_;
   if (n > 0) {
     issue(0, 0);
@@ -1350,17 +1384,25 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     lds_barrier();
     products(0, sa, da);
   }
-  auto step = [&](int it, int ph, f32x16_t& sc, f32x16_t& dc, f32x16_t& sn, f32x16_t& dn) {
+  for (int it = 0; it < n; ++it) {
+    const int ph = it & (NS - 1);
     issue(it + 3, (ph + 3) & (NS - 1));
-    products((ph + 1) & (NS - 1), sn, dn);  // past the last item: a reloaded tile, unused
-    update(ph, it, sc, dc);
+    float x[16], y[16];
+    if constexpr (D <= 64) {
+      consume(ph, sa, da, x, y);
+      __builtin_amdgcn_sched_barrier(0);
+      products((ph + 1) & (NS - 1), sa, da);  // past the last item: a reloaded tile, unused
+    } else {
+      products((ph + 1) & (NS - 1), sb, db_);
+      consume(ph, sa, da, x, y);
+    }
+    update(ph, it, x, y);
     vm_wait<NL>();
     lds_barrier();
-  };
-  for (int it = 0; it < n; ++it) {
-    step(it, it & (NS - 1), sa, da, sb, db_);
-    sa = sb;
-    da = db_;
+    if constexpr (D > 64) {
+      sa = sb;
+      da = db_;
+    }
   }
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
