@@ -33,7 +33,8 @@ struct WorkPos {
 // Padded layouts: the q tile index is outermost and reversed (longest tiles first under a
 // causal mask), (batch, head) fastest.  Workgroups are dispatched to the 8 XCDs round-robin,
 // so when batch * heads is a multiple of 8 every tile of one head runs on the same XCD and
-// shares its K/V rows through that XCD's L2.
+// shares its K/V rows through that XCD's L2.  When every tile costs the same, each XCD
+// instead walks its own heads one after the other (fewer heads resident per XCD).
 __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_tile, WorkPos& w) {
   const Shape& s = p.s;
   if (s.thd) {
@@ -47,8 +48,24 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_til
   }
   int bh = s.batch * s.hq;
   int nt = (s.sq + rows_per_tile - 1) / rows_per_tile;
-  int t = blockIdx.x / bh;
-  int r = blockIdx.x % bh;
+  int t, r;
+  // every q tile sees all sk keys (no window bound cuts any tile's range, no block mask)
+  const int64_t off = s.bottom_right ? int64_t(s.sk) - s.sq : 0;
+  const bool uniform = !s.bm.bits && int64_t(s.sq) - 1 + off + s.lo_rel <= 0 &&
+                       int64_t(s.hi_rel) + off >= int64_t(s.sk) - 1;
+  if (kFwdXcdOrder && uniform && bh % kXcds == 0) {
+    // Tiles of equal cost: XCD x (block b runs on XCD b % 8) owns the (batch, head) pairs
+    // [x per, (x + 1) per), so the q heads of one kv group share an XCD, and walks them
+    // pair after pair: the workgroups resident on an XCD at one time then cover a few
+    // heads, whose K/V rows stay in that XCD's L2.  (Under causal or window masks the
+    // longest-first order over the whole grid, below, balances the CUs better.)
+    const int per = bh / kXcds, x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+    r = x * per + k / nt;
+    t = k % nt;
+  } else {
+    t = blockIdx.x / bh;
+    r = blockIdx.x % bh;
+  }
   w.b = r / s.hq;
   w.h = r % s.hq;
   w.tile = nt - 1 - t;

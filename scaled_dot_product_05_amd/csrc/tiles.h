@@ -38,6 +38,13 @@ constexpr int kFwdBNP = SDPA_FWD_BNP;  // keys per K/V tile, pipelined 16-bit ke
 #define SDPA_FWD_NS_D128 2
 #endif
 constexpr int kFwdStages = SDPA_FWD_NS;            // K/V LDS slots, head_dim <= 64
+#ifndef SDPA_FWD_XCD_ORDER
+#define SDPA_FWD_XCD_ORDER 1
+#endif
+constexpr int kXcds = 8;  // workgroups go to the XCDs round-robin by block index
+// padded-layout forward grids: each XCD walks its own (batch, head) pairs one after the
+// other (0: q tile outermost, (batch, head) fastest)
+constexpr bool kFwdXcdOrder = SDPA_FWD_XCD_ORDER;
 constexpr int kFwdStagesD128 = SDPA_FWD_NS_D128;  // K/V LDS slots, head_dim 128
 #ifndef SDPA_FWD_WIDE_D64
 #define SDPA_FWD_WIDE_D64 0
