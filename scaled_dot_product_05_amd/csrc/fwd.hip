@@ -53,15 +53,15 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_til
   const int64_t off = s.bottom_right ? int64_t(s.sk) - s.sq : 0;
   const bool uniform = !s.bm.bits && int64_t(s.sq) - 1 + off + s.lo_rel <= 0 &&
                        int64_t(s.hi_rel) + off >= int64_t(s.sk) - 1;
-  if (kFwdXcdOrder && uniform && bh % kXcds == 0) {
-    // Tiles of equal cost: XCD x (block b runs on XCD b % 8) owns the (batch, head) pairs
-    // [x per, (x + 1) per), so the q heads of one kv group share an XCD, and walks them
-    // pair after pair: the workgroups resident on an XCD at one time then cover a few
-    // heads, whose K/V rows stay in that XCD's L2.  (Under causal or window masks the
-    // longest-first order over the whole grid, below, balances the CUs better.)
+  if (kFwdXcdOrder && bh % kXcds == 0) {
+    // XCD x (block b runs on XCD b % 8) owns the (batch, head) pairs [x per, (x + 1) per),
+    // so the q heads of one kv group share an XCD and its L2.  Tiles of equal cost: the XCD
+    // walks its pairs one after the other, so the workgroups resident at one time cover a
+    // few heads.  Otherwise (causal or window masks) its tiles go longest first across its
+    // pairs, which balances the CUs better.
     const int per = bh / kXcds, x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-    r = x * per + k / nt;
-    t = k % nt;
+    r = x * per + (uniform ? k / nt : k % per);
+    t = uniform ? k % nt : k / per;
   } else {
     t = blockIdx.x / bh;
     r = blockIdx.x % bh;
