@@ -296,6 +296,11 @@ int check_desc(const sdpa_desc_t* d, Shape* s) {
   s->lo_rel = d->window_left == -1 ? -kUnbounded : clamp_rel(-int64_t(d->window_left));
   s->hi_rel = d->window_right == -1 ? kUnbounded : clamp_rel(int64_t(d->window_right));
   s->bottom_right = d->diag_align == SDPA_ALIGN_BOTTOM_RIGHT;
+  {
+    const int64_t off = s->bottom_right ? int64_t(s->sk) - s->sq : 0;
+    s->uniform = !thd && !s->bm.bits && int64_t(s->sq) - 1 + off + s->lo_rel <= 0 &&
+                 int64_t(s->hi_rel) + off >= int64_t(s->sk) - 1;
+  }
   s->scale = d->softmax_scale;
   s->scale_log2 = float(double(d->softmax_scale) * 1.4426950408889634);
   return SDPA_OK;

@@ -50,9 +50,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_til
   int nt = (s.sq + rows_per_tile - 1) / rows_per_tile;
   int t, r;
   // every q tile sees all sk keys (no window bound cuts any tile's range, no block mask)
-  const int64_t off = s.bottom_right ? int64_t(s.sk) - s.sq : 0;
-  const bool uniform = !s.bm.bits && int64_t(s.sq) - 1 + off + s.lo_rel <= 0 &&
-                       int64_t(s.hi_rel) + off >= int64_t(s.sk) - 1;
+  const bool uniform = s.uniform != 0;
   if (kFwdXcdOrder && bh % kXcds == 0) {
     // XCD x (block b runs on XCD b % 8) owns the (batch, head) pairs [x per, (x + 1) per),
     // so the q heads of one kv group share an XCD and its L2.  Tiles of equal cost: the XCD
@@ -60,8 +58,9 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_til
     // few heads.  Otherwise (causal or window masks) its tiles go longest first across its
     // pairs, which balances the CUs better.
     const int per = bh / kXcds, x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-    r = x * per + (uniform ? k / nt : k % per);
-    t = uniform ? k % nt : k / per;
+    const int dv = uniform ? nt : per, q = k / dv, m = k - q * dv;  // one division
+    r = x * per + (uniform ? q : m);
+    t = uniform ? m : q;
   } else {
     t = blockIdx.x / bh;
     r = blockIdx.x % bh;

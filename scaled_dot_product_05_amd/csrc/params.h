@@ -51,6 +51,7 @@ struct Shape {
   int64_t total_q, total_k;
   int32_t lo_rel, hi_rel;
   int32_t bottom_right;
+  int32_t uniform;   // padded layout, no block mask, and every query row may see all sk keys
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   BlockMaskP bm;

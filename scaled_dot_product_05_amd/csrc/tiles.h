@@ -89,6 +89,12 @@ constexpr int kBwdShortRows = SDPA_BWD_SHORT_ROWS;
 #endif
 constexpr int kBwdSplit = SDPA_BWD_SPLIT;
 constexpr int kBwdSplitPerCU = 8;  // ... when the grid has at most this many blocks per CU
+#ifndef SDPA_BWD_XCD_ORDER
+#define SDPA_BWD_XCD_ORDER 1
+#endif
+// padded-layout backward grids: each XCD owns a contiguous range of (batch, head) pairs
+// (0: tile outermost, (batch, head) fastest)
+constexpr bool kBwdXcdOrder = SDPA_BWD_XCD_ORDER;
 
 // THD scheduler buckets (costs above the last bucket share it)
 constexpr int kSchedBuckets = 4096;
