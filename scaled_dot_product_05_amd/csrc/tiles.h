@@ -45,6 +45,12 @@ constexpr int kXcds = 8;  // workgroups go to the XCDs round-robin by block inde
 // padded-layout forward grids: each XCD walks its own (batch, head) pairs one after the
 // other (0: q tile outermost, (batch, head) fastest)
 constexpr bool kFwdXcdOrder = SDPA_FWD_XCD_ORDER;
+#ifndef SDPA_FWD_HEAD_GROUP
+#define SDPA_FWD_HEAD_GROUP 4
+#endif
+// causal/window forward grids with more than this many pairs per XCD: the XCD takes its
+// pairs in groups of this many, tiles longest first within a group (0: one group)
+constexpr int kFwdHeadGroup = SDPA_FWD_HEAD_GROUP;
 constexpr int kFwdStagesD128 = SDPA_FWD_NS_D128;  // K/V LDS slots, head_dim 128
 #ifndef SDPA_FWD_WIDE_D64
 #define SDPA_FWD_WIDE_D64 0
