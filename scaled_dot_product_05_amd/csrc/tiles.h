@@ -101,6 +101,11 @@ constexpr int kBwdSplitPerCU = 8;  // ... when the grid has at most this many bl
 // padded-layout backward grids: each XCD owns a contiguous range of (batch, head) pairs
 // (0: tile outermost, (batch, head) fastest)
 constexpr bool kBwdXcdOrder = SDPA_BWD_XCD_ORDER;
+#ifndef SDPA_BWD_HEAD_GROUP
+#define SDPA_BWD_HEAD_GROUP 4
+#endif
+// head_dim 128 backward, causal/window grids: kv heads per group of the XCD order (0: none)
+constexpr int kBwdHeadGroup = SDPA_BWD_HEAD_GROUP;
 
 // THD scheduler buckets (costs above the last bucket share it)
 constexpr int kSchedBuckets = 4096;
