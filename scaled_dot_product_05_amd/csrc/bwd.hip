@@ -91,7 +91,8 @@ struct BwdPos {
   int b, h, tile;
 };
 
-// GROUPED (head_dim 128 kernels): causal/window grids with more than kBwdHeadGroup kv heads'
+// GROUPED (head_dim 128 kernels): THD grids with a multiple of 8 heads give each XCD a
+// contiguous range of heads; causal/window grids with more than kBwdHeadGroup kv heads'
 // pairs per XCD take them in groups of kBwdHeadGroup (q heads: times the GQA group), tiles
 // longest first within a group (measured: B8 S4096 D128 2596 -> 2520 us, B16 S2048 D128
 // 1571 -> 1474 us; at head_dim 64 it lost 1-5%).
@@ -101,8 +102,19 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
                                            bool reverse, BwdPos& w, int bid = -1) {
   if (bid < 0) bid = blockIdx.x;
   if (s.thd) {
-    int item = bid / heads;
-    w.h = bid % heads;
+    int item, h;
+    if (GROUPED && kBwdXcdOrder && heads % kXcds == 0) {
+      // XCD x (block b on XCD b % 8) runs the contiguous heads [x per, (x + 1) per), so a kv
+      // group's q heads share an XCD (head_dim 128 kernels; C4's THD GQA backward
+      // 1045 -> 988 us)
+      const int per = heads / kXcds, j = bid / kXcds;
+      item = j / per;
+      h = (bid % kXcds) * per + j % per;
+    } else {
+      item = bid / heads;
+      h = bid % heads;
+    }
+    w.h = h;
     if (item >= *count) return false;
     WorkItem it = work[item];
     w.b = it.seq;

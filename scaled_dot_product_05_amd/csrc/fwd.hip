@@ -38,8 +38,18 @@ struct WorkPos {
 __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_tile, WorkPos& w) {
   const Shape& s = p.s;
   if (s.thd) {
-    int item = blockIdx.x / s.hq;
-    w.h = blockIdx.x % s.hq;
+    int item, h;
+    if (kFwdXcdOrder && s.hq % kXcds == 0) {
+      // XCD x (block b on XCD b % 8) runs the contiguous q heads [x per, (x + 1) per), so
+      // the q heads of one kv group share an XCD's L2
+      const int per = s.hq / kXcds, j = blockIdx.x / kXcds;
+      item = j / per;
+      h = (blockIdx.x % kXcds) * per + j % per;
+    } else {
+      item = blockIdx.x / s.hq;
+      h = blockIdx.x % s.hq;
+    }
+    w.h = h;
     if (item >= *p.work_count) return false;
     WorkItem it = p.work[item];
     w.b = it.seq;
