@@ -123,7 +123,7 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
   }
   int bh = s.batch * heads;
   int nt = (len + tile_rows - 1) / tile_rows;
-  int t, r;
+  int t = 0, r = 0;
   const bool uniform = s.uniform != 0;
   bool grouped = false;
   if constexpr (GROUPED) {
