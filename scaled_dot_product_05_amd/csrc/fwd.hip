@@ -30,11 +30,13 @@ struct WorkPos {
 };
 
 // Decode blockIdx.x into (sequence, q head, q tile).  Returns false for idle blocks.
-// Padded layouts: the q tile index is outermost and reversed (longest tiles first under a
-// causal mask), (batch, head) fastest.  Workgroups are dispatched to the 8 XCDs round-robin,
-// so when batch * heads is a multiple of 8 every tile of one head runs on the same XCD and
-// shares its K/V rows through that XCD's L2.  When every tile costs the same, each XCD
-// instead walks its own heads one after the other (fewer heads resident per XCD).
+// Workgroups are dispatched to the 8 XCDs round-robin (block b on XCD b % 8).  Padded
+// layouts with batch * heads a multiple of 8: each XCD owns a contiguous range of
+// (batch, head) pairs and takes its tiles longest first (reversed q tile index), in groups
+// of kFwdHeadGroup pairs when it owns more, or pair after pair when every tile costs the
+// same.  Otherwise the q tile index is outermost (longest first), (batch, head) fastest.
+// THD: the scheduler's cost-sorted items, with contiguous q-head ranges per XCD when the
+// head count is a multiple of 8.
 __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_tile, WorkPos& w) {
   const Shape& s = p.s;
   if (s.thd) {
