@@ -28,10 +28,12 @@ def e4m3_decode(codes) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
-def fp8_forward(q8, k8, v8, descale_q, descale_k, descale_v, scale, mask=None):
+def fp8_forward(q8, k8, v8, descale_q, descale_k, descale_v, scale, mask=None,
+                return_p=False):
     """O, LSE of attention on q8 * descale_q, k8 * descale_k, v8 * descale_v (E4M3 codes,
-    [B,H,S,D]); ``mask`` as in attention_forward."""
+    [B,H,S,D]); ``mask`` as in attention_forward; with ``return_p`` also the softmax
+    weights P [B,Hq,Sq,Sk]."""
     q = e4m3_decode(q8) * float(descale_q)
     k = e4m3_decode(k8) * float(descale_k)
     v = e4m3_decode(v8) * float(descale_v)
-    return attention_forward(q, k, v, scale, mask)
+    return attention_forward(q, k, v, scale, mask, return_p=return_p)

@@ -515,12 +515,14 @@ __global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) 
 
   f32x16_t acc[QB][NDB];
   float m_run[QB], l_run[QB];
+  bool live[QB];  // the lane's row lies inside the sequence
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[j][i] = zero16();
     m_run[j] = kNegInf;
     l_run[j] = 0.f;
+    live[j] = qw0 + 32 * j + l32 < g.sq;
   }
 
   // The key blocks and query blocks are independent accumulation chains; alternating them
@@ -595,8 +597,12 @@ __global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) 
   // exponentiated against the current m_run with no max taken; the per-lane partial sums,
   // which are needed anyway, then show whether that was safe: every P is at most its lane's
   // sum, so a sum <= kSumMax bounds every P by 2^13 (fp16 P stays finite).  Only a lane
-  // whose sum is larger (or not finite), or a row with no reference yet that sees a key,
-  // sends the wave through the max and rescale below and a second exponentiation.
+  // whose sum is larger (or not finite), or a live row with no reference yet, sends the
+  // wave through the max and rescale below and a second exponentiation.  The second case
+  // cannot be read off the sum: when every visible score of the row lies ~126 (log2 units)
+  // or more below 0, exp2 against the stand-in reference 0 underflows to a zero sum, and
+  // the row would keep no reference and lose its keys.  A row's first tile with a visible
+  // key therefore always takes the max; rows past the sequence end never do.
   constexpr float kSumMax = 8192.f;
   auto softmax_ref = [&](const f32x16_t(&st)[QB][NKB]) {
 #pragma unroll
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) 
     probs(st, pf, ps);
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < QB; ++j) bad = bad || (m_run[j] == kNegInf ? ps[j] > 0.f : !(ps[j] <= kSumMax));
+    for (int j = 0; j < QB; ++j) bad = bad || (m_run[j] == kNegInf ? live[j] : !(ps[j] <= kSumMax));
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       softmax_ref(st);
       probs(st, pf, ps);

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 WINDOWS = [((-1, -1), 0), ((-1, 0), 0), ((3, 2), 0), ((-1, 0), 1), ((40, 0), 1), ((-1, -129), 0)]
 
 
-def run_case(w, backward=True, dlse=False):
+def run_case(w, backward=True, dlse=False, zero_exact=()):
     say(f"case {w.name} {w.dtype} {w.layout} B={w.batch} Sq={w.seqlen_q} Sk={w.seqlen_k} "
         f"Hq={w.heads_q} Hk={w.heads_kv} D={w.head_dim} win={w.window} al={w.diag_align}")
     q, k, v = to_dev(w)
@@ -34,7 +34,7 @@ def run_case(w, backward=True, dlse=False):
     dq, dk, dv = gpu_backward(w, q, k, v, o, lse, w.dout.to(DEV), dl_dev, cq, ck)
     torch.cuda.synchronize()
     refs = oracle_backward(w, synth.f64(w.dlse) if dl_dev is not None else None)
-    check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], refs, w.dtype, "bwd")
+    check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], refs, w.dtype, "bwd", zero_exact)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -77,8 +77,9 @@ def test_thd_cross_lengths_bottom_right():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_single_key_and_single_query(dtype):
+    # one key: P = 1 and dP = Delta, so dS = 0 and dQ, dK vanish in exact arithmetic
     run_case(synth.dense(16, 500, dtype, "bshd", 3, 77, 1, 2, 2, 64, 0.5, name="sk1",
-                         with_grad=True))
+                         with_grad=True), zero_exact=("dq", "dk"))
     run_case(synth.dense(17, 501, dtype, "bshd", 3, 1, 77, 2, 2, 64, 0.5, name="sq1",
                          with_grad=True))
 
@@ -102,6 +103,54 @@ def test_extreme_scores_stay_finite():
                     with_grad=True, name="big_scores")
     w.q = (w.q.float() * 3).half()
     run_case(w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("window,align", [((-1, 0), 0), ((40, 0), 1), ((-1, -1), 0)])
+def test_very_negative_scores_keep_their_keys(dtype, window, align):
+    # q rows near +1 and k rows near -1, scale 2: every score lies near -128 (natural log),
+    # so exp2 of a score against a reference of 0 underflows to 0 for every key.  Each row
+    # must still take its own maximum as reference: finite LSE, O a weighted mean of V.
+    # Row 0 of the causal case sees a single key.
+    w = synth.dense(23, 950, dtype, "bshd", 1, 200, 200, 2, 2, 64, 2.0, window, align,
+                    with_grad=True, with_dlse=True, name="neg_scores")
+    zq = synth.normal(23, 950, 10, (1, 200, 2, 64))
+    zk = synth.normal(23, 950, 11, (1, 200, 2, 64))
+    w.q = synth.cast(1.0 + 0.1 * np.abs(zq), dtype)
+    w.k = synth.cast(-(1.0 + 0.1 * zk), dtype)
+    run_case(w, dlse=True)
+    s_max = 2.0 * float((synth.f64(w.q)[0, :, 0] @ synth.f64(w.k)[0, :, 0].T).max())
+    assert s_max < -100.0, s_max
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_broadcast_kv_with_zero_strides(dtype):
+    # inputs may carry stride 0: K repeated over the kv heads (head stride 0) and V shared by
+    # every batch (batch stride 0); the result must be the oracle's on the repeated values
+    # and bitwise the result on materialised copies; dK, dV are per-head gradients
+    b, s, hq, hk, d = 3, 200, 8, 4, 64
+    w = synth.dense(24, 960, dtype, "bshd", b, s, s, hq, hk, d, 0.125, (-1, 0), with_grad=True,
+                    name="stride0")
+    kb = w.k[:, :, :1]
+    vb = w.v[:1]
+    w.k = kb.expand(b, s, hk, d)
+    w.v = vb.expand(b, s, hk, d)
+    say(f"case stride-0 {dtype}")
+    q = w.q.to(DEV)
+    k = kb.to(DEV).expand(b, s, hk, d)
+    v = vb.to(DEV).expand(b, s, hk, d)
+    assert k.stride()[2] == 0 and v.stride()[0] == 0
+    o, lse = gpu_forward(w, q, k, v)
+    torch.cuda.synchronize()
+    check_forward(gpu_bhsd(o, w), synth.f64(lse), *oracle_forward(w), dtype, "stride-0 fwd")
+    oc, lc = gpu_forward(w, q, k.contiguous(), v.contiguous())
+    assert torch.equal(o, oc) and torch.equal(lse, lc)
+    g = w.dout.to(DEV)
+    grads = gpu_backward(w, q, k, v, o, lse, g)
+    check_grads([gpu_bhsd(t, w) for t in grads], oracle_backward(w), dtype, "stride-0 bwd")
+    grads_c = gpu_backward(w, q, k.contiguous(), v.contiguous(), o, lse, g)
+    for a, c in zip(grads, grads_c):
+        assert torch.equal(a, c)
 
 
 def test_unaligned_rows_take_the_element_path():

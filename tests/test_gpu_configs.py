@@ -15,18 +15,22 @@ from gpu_util import (DEV, G_TOL, O_TOL, check_forward, check_grads, cu_dev, gpu
 
 pytestmark = pytest.mark.gpu
 
+SEEDS = [0, 1, 2]  # the pages' five workloads at the default seed and two more
 
-def test_c1_fp32_noncausal_bhsd():
-    w = synth.c1()
-    say("case c1")
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_c1_fp32_noncausal_bhsd(seed):
+    w = synth.c1(seed)
+    say(f"case c1 seed={seed}")
     q, k, v = to_dev(w)
     o, lse = gpu_forward(w, q, k, v)
     check_forward(gpu_bhsd(o, w), synth.f64(lse), *oracle_forward(w), "f32", "c1")
 
 
-def test_c2_bf16_causal_fwd_bwd():
-    w = synth.c2()
-    say("case c2")
+@pytest.mark.parametrize("seed", SEEDS)
+def test_c2_bf16_causal_fwd_bwd(seed):
+    w = synth.c2(seed)
+    say(f"case c2 seed={seed}")
     q, k, v = to_dev(w)
     o, lse = gpu_forward(w, q, k, v)
     check_forward(gpu_bhsd(o, w), synth.f64(lse), *oracle_forward(w), "bf16", "c2 fwd")
@@ -34,10 +38,11 @@ def test_c2_bf16_causal_fwd_bwd():
     check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], oracle_backward(w), "bf16", "c2 bwd")
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("scale", [1.0, 0.1])
-def test_c3_fp16_packed_mqa_views(scale):
-    w = synth.c3(scale=scale)
-    say(f"case c3 scale={scale}")
+def test_c3_fp16_packed_mqa_views(scale, seed):
+    w = synth.c3(seed, scale=scale)
+    say(f"case c3 scale={scale} seed={seed}")
     q, k, v = to_dev(w)
     assert not q.is_contiguous() and q.stride() == (1152, 1152, 64, 1)
     o, lse = gpu_forward(w, q, k, v)
@@ -51,9 +56,10 @@ def test_c3_fp16_packed_mqa_views(scale):
     assert torch.equal(ob.permute(2, 0, 1, 3), o) and torch.equal(lb, lse)
 
 
-def test_c4_thd_gqa_fwd_full_and_bwd():
-    w = synth.c4()
-    say(f"case c4 lengths={np.diff(w.cu_seqlens_q).tolist()}")
+@pytest.mark.parametrize("seed", SEEDS)
+def test_c4_thd_gqa_fwd_full_and_bwd(seed):
+    w = synth.c4(seed)
+    say(f"case c4 seed={seed} lengths={np.diff(w.cu_seqlens_q).tolist()}")
     q, k, v = to_dev(w)
     cq, ck = cu_dev(w)
     o, lse = gpu_forward(w, q, k, v, cq, ck)
@@ -145,8 +151,8 @@ def test_merge_kernels(dtype, d):
     assert (got[1][0, 0, 3:5] == 0).all() and (got[3][0, 0, 3:5] == 0).all()
 
 
-def _c5_device():
-    c = synth.c5()
+def _c5_device(seed=0):
+    c = synth.c5(seed)
     qkv = c["qkv"].to(DEV)
     da = c["heads"] * c["d"]
     q = qkv[:, :, :da].unflatten(2, (c["heads"], c["d"]))
@@ -155,10 +161,11 @@ def _c5_device():
     return c, q, k, v
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("upstream", ["ones", "random"])
-def test_c5_local_global_merge_fwd_bwd(upstream):
-    c, q, k, v = _c5_device()
-    say(f"case c5 upstream={upstream}")
+def test_c5_local_global_merge_fwd_bwd(upstream, seed):
+    c, q, k, v = _c5_device(seed)
+    say(f"case c5 upstream={upstream} seed={seed}")
     sc, ng = c["scale"], c["global_keys"]
     ol, ll = S.forward(q, k, v, "bshd", sc, c["local_window"])
     og, lg = S.forward(q, k[:, :ng], v[:, :ng], "bshd", sc, (-1, 0))

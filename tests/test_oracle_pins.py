@@ -275,6 +275,145 @@ def test_backward_identities():
     assert lhs == pytest.approx(rhs, abs=1e-11)
 
 
+def _torch_attention_with_lse(q, k, v, scale, vis):
+    """PyTorch float64 SDPA (boolean mask, K/V expanded to the q heads) plus the LSE as
+    torch.logsumexp of the masked scores; every row of ``vis`` must see a key.  Returns
+    the leaf tensors too, for autograd."""
+    g = q.shape[1] // k.shape[1]
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    tm = torch.tensor(np.broadcast_to(vis, (q.shape[0], q.shape[1], q.shape[2], k.shape[2])).copy())
+    ke, ve = tk.repeat_interleave(g, 1), tv.repeat_interleave(g, 1)
+    out = F.scaled_dot_product_attention(tq, ke, ve, attn_mask=tm, scale=scale)
+    sc = (scale * tq @ ke.transpose(-1, -2)).masked_fill(~tm, -math.inf)
+    return out, torch.logsumexp(sc, -1), (tq, tk, tv)
+
+
+def _random_element_mask(seed, shape, window, align, density=0.6):
+    """Random boolean element bits [B,H,Sq,Sk]; each row keeps one key that the window admits
+    (so every row of mask AND window sees a key and PyTorch's SDPA is defined)."""
+    rng = np.random.default_rng(seed)
+    m = rng.random(shape) < density
+    wm = window_mask(shape[2], shape[3], window[0], window[1], align)
+    assert wm.any(1).all()
+    first = wm.argmax(1)
+    m[..., np.arange(shape[2]), first] = True
+    return m
+
+
+@pytest.mark.parametrize("window,align,sq,sk", [((3, 2), 0, 11, 13), ((-1, 0), 1, 9, 14),
+                                                ((-1, -129), 1, 7, 140), ((-1, -1), 0, 8, 10)])
+def test_masked_forward_backward_match_torch(window, align, sq, sk):
+    # the block-sparse path's result: element bits AND the window, against PyTorch float64
+    # SDPA and autograd under (bits & window); dropping either side of the AND fails here
+    hq, hk, d, scale = 4, 2, 6, 0.45
+    q, k, v = rnd(160, 2, hq, sq, d), rnd(161, 2, hk, sk, d), rnd(162, 2, hk, sk, d)
+    g, gl = rnd(163, 2, hq, sq, d), rnd(164, 2, hq, sq)
+    bits = _random_element_mask(165, (2, hq, sq, sk), window, align)
+    vis = bits & window_mask(sq, sk, window[0], window[1], align)
+    assert not (vis == bits).all() or window == (-1, -1)
+    o, lse = oracle.masked_forward(q, k, v, scale, bits, window, align)
+    out, tl, (tq, tk, tv) = _torch_attention_with_lse(q, k, v, scale, vis)
+    assert np.abs(o - out.detach().numpy()).max() < 1e-13
+    assert np.abs(lse - tl.detach().numpy()).max() < 1e-13
+    dq, dk, dv = oracle.masked_backward(q, k, v, g, scale, bits, window, align, dlse=gl)
+    ((out * torch.tensor(g)).sum() + (tl * torch.tensor(gl)).sum()).backward()
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-12
+
+
+def test_masked_rows_without_keys_are_zero():
+    # element bits that leave rows 1 and 4 empty (and key 2 never visible): O = 0,
+    # LSE = -inf, no gradient on those rows, none into the invisible key
+    q, k, v = rnd(170, 1, 2, 6, 4), rnd(171, 1, 2, 7, 4), rnd(172, 1, 2, 7, 4)
+    bits = np.ones((6, 7), bool)
+    bits[[1, 4]] = False
+    bits[:, 2] = False
+    o, lse = oracle.masked_forward(q, k, v, 0.8, bits, (-1, -1))
+    assert (o[:, :, [1, 4]] == 0).all() and np.isneginf(lse[:, :, [1, 4]]).all()
+    assert np.isfinite(lse[:, :, [0, 2, 3, 5]]).all()
+    dq, dk, dv = oracle.masked_backward(q, k, v, rnd(173, 1, 2, 6, 4), 0.8, bits, (-1, -1),
+                                        dlse=rnd(174, 1, 2, 6))
+    assert (dq[:, :, [1, 4]] == 0).all() and (dk[:, :, 2] == 0).all() and (dv[:, :, 2] == 0).all()
+
+
+def test_backward_random_mask_finite_differences():
+    # attention_backward with an arbitrary boolean mask (one row fully masked), against
+    # central differences of L = sum(O g) + sum(LSE gl) over rows with a visible key
+    hq, hk, sq, sk, d, scale = 2, 1, 5, 6, 3, 0.9
+    q, k, v = rnd(175, 1, hq, sq, d), rnd(176, 1, hk, sk, d), rnd(177, 1, hk, sk, d)
+    g, gl = rnd(178, 1, hq, sq, d), rnd(179, 1, hq, sq)
+    mask = np.random.default_rng(180).random((1, hq, sq, sk)) < 0.5
+    mask[0, 0, 2] = False
+    mask[0, 1, 3] = False
+    mask[0, 1, 3, 4] = True
+    dq, dk, dv = attention_backward(q, k, v, g, scale, mask, dlse=gl)
+    h = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = _loss(q, k, v, scale, mask, g, gl)
+            arr[idx] = old - h
+            lm = _loss(q, k, v, scale, mask, g, gl)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.abs(num - grad).max() < 1e-7 * max(1.0, np.abs(grad).max())
+    assert (dq[0, 0, 2] == 0).all()
+
+
+def test_backward_random_mask_matches_torch_autograd():
+    hq, hk, sq, sk, d, scale = 4, 2, 12, 9, 5, 0.35
+    q, k, v = rnd(181, 2, hq, sq, d), rnd(182, 2, hk, sk, d), rnd(183, 2, hk, sk, d)
+    g, gl = rnd(184, 2, hq, sq, d), rnd(185, 2, hq, sq)
+    mask = _random_element_mask(186, (2, hq, sq, sk), (-1, -1), 0, density=0.4)
+    dq, dk, dv = attention_backward(q, k, v, g, scale, mask, dlse=gl)
+    out, tl, (tq, tk, tv) = _torch_attention_with_lse(q, k, v, scale, mask)
+    ((out * torch.tensor(g)).sum() + (tl * torch.tensor(gl)).sum()).backward()
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-12
+
+
+@pytest.mark.parametrize("align", [1, 0])
+def test_thd_cross_lengths_match_torch_per_sequence(align):
+    # packed varlen with cu_seqlens_k != cu_seqlens_q: sequence s is its own problem of
+    # Lq_s queries and Lk_s keys; causal aligned bottom-right (query i sees key j iff
+    # j <= i + Lk - Lq) or top-left (j <= i).  Reference: PyTorch float64 SDPA per sequence
+    # with the mask built by torch.tril; a sequence with no keys gives O = 0, LSE = -inf.
+    lq, lk = [4, 7, 3, 5, 2], [6, 3, 3, 0, 9]
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    hq, hk, d, scale = 4, 2, 5, 0.55
+    rng = np.random.default_rng(187)
+    q, g = rng.standard_normal((cq[-1], hq, d)), rng.standard_normal((cq[-1], hq, d))
+    k, v = rng.standard_normal((ck[-1], hk, d)), rng.standard_normal((ck[-1], hk, d))
+    gl = rng.standard_normal((hq, cq[-1]))
+    o, lse = oracle.thd_forward(q, k, v, cq, ck, scale, (-1, 0), align)
+    dq, dk, dv = oracle.thd_backward(q, k, v, g, cq, ck, scale, (-1, 0), align, dlse=gl)
+    for s_ in range(len(lq)):
+        a, b = cq[s_], cq[s_ + 1]
+        c, e = ck[s_], ck[s_ + 1]
+        diag = (lk[s_] - lq[s_]) if align else 0
+        vis = torch.ones(lq[s_], lk[s_], dtype=torch.bool).tril(diagonal=diag).numpy()
+        rows = vis.any(1)
+        assert (o[a:b][~rows] == 0).all() and np.isneginf(lse[:, a:b][:, ~rows]).all()
+        assert (dq[a:b][~rows] == 0).all()
+        if not rows.any():
+            continue
+        sel = np.flatnonzero(rows)
+        bh = lambda t, lo, hi: t[lo:hi].transpose(1, 0, 2)[None]
+        out, tl, (tq, tk, tv) = _torch_attention_with_lse(bh(q, a, b)[:, :, sel], bh(k, c, e),
+                                                          bh(v, c, e), scale, vis[sel])
+        assert np.abs(o[a:b][sel] - out.detach().numpy()[0].transpose(1, 0, 2)).max() < 1e-13
+        assert np.abs(lse[:, a:b][:, sel] - tl.detach().numpy()[0]).max() < 1e-13
+        loss = (out * torch.tensor(bh(g, a, b)[:, :, sel])).sum() + \
+            (tl * torch.tensor(gl[:, a:b][:, sel][None])).sum()
+        loss.backward()
+        assert np.abs(dq[a:b][sel] - tq.grad.numpy()[0].transpose(1, 0, 2)).max() < 1e-12
+        assert np.abs(dk[c:e] - tk.grad.numpy()[0].transpose(1, 0, 2)).max() < 1e-12
+        assert np.abs(dv[c:e] - tv.grad.numpy()[0].transpose(1, 0, 2)).max() < 1e-12
+
+
 # ---------------------------------------------------------------------------------------
 # restricted forms used at full size: rows / columns of the same definition
 # ---------------------------------------------------------------------------------------
