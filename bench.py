@@ -1,14 +1,25 @@
 """Throughput of the fused attention hot path on one MI355X.
 
-One step = one pass of the whole path over the causal self-attention workload of the
-pages' bf16 case (B4 S1024 H8 D64, BSHD, scale 1/8): sdpa_fwd (O and LSE) then sdpa_bwd
-(Delta pre-pass, dK/dV, dQ), inputs resident in HBM.  value = algorithmic TFLOP/s of the
-step (forward 4 D per visible pair, backward 10 D).  The same JSON line carries the
-dominant kernel's roofline (live hipEvent timing on its stream), the fp64 oracle timed on
-the host, and extra measurements: the long-sequence causal forward sweep, the packed MQA
-fp16 case, the varlen THD GQA case, the merge kernels and the short-sequence forward.
+One step = one pass of the whole path over one batch of the varlen THD workload (the
+largest of the pages' problem statements that fits one GPU; "Add support for cuDNN
+FusedAttention + THD + CP", TransformerEngine issue 885): 8 causal sequences with lengths
+uniform on [256, 4096], packed with int32 cu_seqlens, 16 q heads over 4 kv heads, head_dim
+128, bf16, scale 1/sqrt(128); sdpa_fwd (O and LSE) then sdpa_bwd (Delta pre-pass, dK/dV and
+dQ), inputs resident in HBM.  value = algorithmic TFLOP/s of the median step (forward
+4 D per visible pair, backward 10 D).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+Timing follows the pages' benchmark table (RETURNN PR 1798: warm-up steps discarded, then
+min / median / mean / stddev / rounds): W warm-up steps, a timed region of exactly K steps
+bracketed by device synchronisations, then a statistics pass with one hipEvent pair per
+step over at least 100 steps and 200 ms, during which the shader clock is sampled.  The
+same JSON line carries the dominant kernel's roofline (per-launch hipEvents recorded by the
+library on its launch stream), the fp64 oracle timed on the host on a bounded sample of
+the step, and extra measurements: the long-sequence causal forward sweep, the pages' bf16
+C2 case, fp32, the packed MQA fp16 case, block-sparse masks, FP8, the merge kernels and
+short sequences.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                       [--no-extra]
 """
 from __future__ import annotations
 
@@ -16,6 +27,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import subprocess
 import sys
@@ -79,20 +91,142 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
+def step_stats(torch, fn, rounds):
+    """Per-call hipEvent pairs on the current stream (the stream the library launches on)
+    around ``rounds`` back-to-back calls: min / median / mean / stddev / rounds in ms."""
+    import statistics
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(rounds)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    return {"min_ms": round(min(t), 5), "median_ms": round(statistics.median(t), 5),
+            "mean_ms": round(statistics.fmean(t), 5),
+            "stddev_ms": round(statistics.pstdev(t), 5), "rounds": rounds}
+
+
+def stat_rounds(ms_est, lo=100, min_ms=200.0, hi=5000):
+    """At least ``lo`` calls and at least ``min_ms`` of GPU time."""
+    return int(min(hi, max(lo, math.ceil(min_ms / max(ms_est, 1e-4)))))
+
+
+class ClockSampler:
+    """Samples the GPU shader clock while a timed region runs: the current sclk level of
+    the device's DPM table in sysfs (the value rocm-smi reports), every 25 ms."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self.stop = threading.Event()
+        self.th = threading.Thread(target=self._run, daemon=True)
+
+    def read(self):
+        for p in self.paths:
+            try:
+                with open(p) as f:
+                    for line in f:
+                        if "*" in line:
+                            return float(line.split(":")[1].strip().split("M")[0].strip("( "))
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = self.read()
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(0.025)
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.th.join()
+
+    def summary(self):
+        import statistics
+        if not self.samples:
+            return {"source": "sysfs pp_dpm_sclk", "samples": 0, "median_mhz": None}
+        return {"source": "sysfs pp_dpm_sclk (current level), sampled every 25 ms during the "
+                          "statistics pass", "samples": len(self.samples),
+                "median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples)}
+
+
+class Step:
+    """One pass of the hot path over one batch of a workload, inputs resident in HBM:
+    sdpa_fwd then (unless forward-only) sdpa_bwd, through the C ABI on the current stream,
+    into preallocated outputs and workspaces."""
+
+    def __init__(self, torch, S, w, dev, fwd_only=False):
+        import numpy as np
+        self.w = w
+        q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+        g = torch.empty_like(q) if fwd_only else w.dout.to(dev)
+        if w.is_thd:
+            self.cu = torch.from_numpy(w.cu_seqlens_q).to(dev)
+            lens = np.diff(w.cu_seqlens_q).astype(np.int64)
+            pr = S.Problem(q, k, "thd", w.scale, w.window, cu_seqlens_q=self.cu,
+                           max_seqlen_q=int(lens.max()))
+            self.nvis = w.heads_q * sum(S.n_visible(int(L), int(L), w.window) for L in lens)
+        else:
+            pr = S.Problem(q, k, w.layout, w.scale, w.window)
+            self.nvis = w.batch * w.heads_q * S.n_visible(w.seqlen_q, w.seqlen_k, w.window)
+        self.pr = pr
+        o = torch.empty_like(q)
+        lse = torch.empty(pr.lse_shape, dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        nf, nb = S.sdpa_fwd_workspace_size(pr.desc), S.sdpa_bwd_workspace_size(pr.desc)
+        self.wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        self.keep = (q, k, v, g, o, lse, dq, dk, dv)
+        self.h = [S.tensor(t) for t in (q, k, v, o, g, dq, dk, dv)]
+        self.hl, self.hnull = S.rowstat(lse), S.rowstat(None)
+        self.wf = (ctypes.c_void_p(self.wsf.data_ptr()) if nf else None, nf)
+        self.wb = (ctypes.c_void_p(self.wsb.data_ptr()) if nb else None, nb)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.lib, self.S, self.fwd_only = S.lib(), S, fwd_only
+        d = w.head_dim
+        self.flops = 4 * d * self.nvis + (0 if fwd_only else 10 * d * self.nvis)
+        # algorithmic flops per launch: forward 4 D per visible pair; backward 10 D, of which
+        # dK/dV (S, dP, dV, dK products) 8 D and dQ 2 D when they run as separate launches
+        self.alg_flops = {"attn_fwd": 4 * d * self.nvis, "bwd_main": 10 * d * self.nvis,
+                          "bwd_dkdv": 8 * d * self.nvis, "bwd_dq": 2 * d * self.nvis}
+
+    def __call__(self):
+        hq, hk, hv, ho, hg, hdq, hdk, hdv = self.h
+        desc = ctypes.byref(self.pr.desc)
+        r1 = self.lib.sdpa_fwd(desc, hq, hk, hv, ho, self.hl, self.wf[0], self.wf[1], self.stream)
+        r2 = 0 if self.fwd_only else self.lib.sdpa_bwd(
+            desc, hq, hk, hv, ho, self.hl, hg, self.hnull, hdq, hdk, hdv, 0, self.wb[0],
+            self.wb[1], self.stream)
+        if r1 or r2:
+            raise self.S.SdpaError(r1 or r2, self.lib.sdpa_last_error().decode())
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra measurements")
-    ap.add_argument("--workload", choices=tuple(MFMA_WORKLOADS) + tuple(HBM_WORKLOADS), default="c2",
-                    help="c2: causal bf16 fwd+bwd B4 S1024 H8 D64 (default); target: causal bf16 "
-                         "forward only, B8 S4096 H8 D64; target_d128: the same forward at H16 "
-                         "D128; target_step: fwd+bwd at B8 S4096 H8 D64 (the last three for "
-                         "profiling the long-sequence kernels); short / merge: the HBM-bound "
-                         "short-sequence forward and merge kernels (for profiling them; the "
-                         "line reports GB/s)")
+    ap.add_argument("--workload", choices=tuple(MFMA_WORKLOADS) + tuple(HBM_WORKLOADS), default="c4",
+                    help="c4 (default): varlen THD causal bf16 fwd+bwd, 8 sequences of "
+                         "U[256,4096] tokens, Hq16/Hk4 D128; c2: causal bf16 fwd+bwd B4 S1024 H8 "
+                         "D64; target / target_d128: causal bf16 forward B8 S4096 H8 D64 / H16 "
+                         "D128; target_step: fwd+bwd B8 S4096 H8 D64; f32_step: causal fp32 "
+                         "fwd+bwd B4 S4096 H8 D64 (these for profiling); short / merge: the "
+                         "HBM-bound short-sequence and merge kernels (the line reports GB/s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
     args = ap.parse_args()
@@ -113,114 +247,98 @@ def main() -> int:
     if args.workload in HBM_WORKLOADS:
         return hbm_main(args, torch, S, synth, dev)
 
-    # ---------------- the step: causal bf16 fwd + bwd, B4 S1024 H8 D64 ----------------
-    fwd_only = args.workload in ("target", "target_d128")
-    w = {"c2": lambda: synth.c2(), "target": lambda: synth.target(),
+    wl = args.workload
+    fwd_only = wl in ("target", "target_d128")
+    w = {"c4": lambda: synth.c4(), "c2": lambda: synth.c2(), "target": lambda: synth.target(),
          "target_d128": lambda: synth.target(h=16, d=128),
-         "target_step": lambda: synth.target(with_grad=True)}[args.workload]()
-    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
-    g = torch.empty_like(q) if fwd_only else w.dout.to(dev)
-    pr = S.Problem(q, k, "bshd", w.scale, w.window)
-    o = torch.empty_like(q)
-    lse = torch.empty(pr.lse_shape, dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(S.sdpa_bwd_workspace_size(pr.desc), dtype=torch.uint8, device=dev)
-    lib = S.lib()
-    hq, hk, hv, ho, hg = (S.tensor(t) for t in (q, k, v, o, g))
-    hdq, hdk, hdv = (S.tensor(t) for t in (dq, dk, dv))
-    hl, hnull = S.rowstat(lse), S.rowstat(None)
-    desc = pr.desc
-    stream = torch.cuda.current_stream().cuda_stream
-    wsp, wsn = ctypes.c_void_p(ws.data_ptr()), ws.numel()
-
-    def step():
-        r1 = lib.sdpa_fwd(ctypes.byref(desc), hq, hk, hv, ho, hl, None, 0, stream)
-        r2 = 0 if fwd_only else lib.sdpa_bwd(ctypes.byref(desc), hq, hk, hv, ho, hl, hg, hnull,
-                                             hdq, hdk, hdv, 0, wsp, wsn, stream)
-        if r1 or r2:
-            raise S.SdpaError(r1 or r2, lib.sdpa_last_error().decode())
-
-    nvis = w.batch * w.heads_q * S.n_visible(w.seqlen_q, w.seqlen_k, w.window)
-    d = w.head_dim
-    flops_step = S.flops(nvis, d) + (0 if fwd_only else S.flops(nvis, d, backward=True))
-    # algorithmic flops per launch: forward 4 D per visible pair; backward 10 D, of which
-    # dK/dV (S, dP, dV, dK products) 8 D and dQ 2 D when they run as separate launches
-    alg_flops = {"attn_fwd": 4 * d * nvis, "bwd_main": 10 * d * nvis, "bwd_dkdv": 8 * d * nvis,
-                 "bwd_dq": 2 * d * nvis}
+         "target_step": lambda: synth.target(with_grad=True),
+         "f32_step": lambda: synth.target(b=4, s=4096, with_grad=True, dtype="f32")}[wl]()
+    step = Step(torch, S, w, dev, fwd_only)
+    dtype = w.dtype
+    peak = PEAK_TFLOPS[dtype]
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Timed region: K steps back to back, bracketed by events on the launch stream and by
-    # the host clock.  No per-launch events inside it (they add a few microseconds each).
+    # Timed region: exactly K steps back to back, bracketed by a device synchronisation and
+    # by events on the launch stream; no per-launch events inside it.
     t0 = time.perf_counter()
     with Timer(torch) as tm:
         for _ in range(args.steps):
             step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    gpu_ms = tm.ms() / args.steps
-    ms_step = max(wall_ms, gpu_ms)
-    value = flops_step / (ms_step * 1e-3) / 1e12
-    log(f"step {ms_step:.4f} ms (wall {wall_ms:.4f}, events {gpu_ms:.4f}) -> {value:.2f} TFLOP/s")
-    # Per-kernel durations: the same K steps again with a hipEvent pair around every launch
-    # (recorded by the library on the stream the kernel runs on).
+    region_ms = max((t1 - t0) * 1e3 / args.steps, tm.ms() / args.steps)
+    # Statistics pass: one event pair per step around at least 100 steps and 200 ms,
+    # while the shader clock is sampled; the median step is the headline.
+    rounds = stat_rounds(region_ms)
+    with ClockSampler() as clk:
+        st = step_stats(torch, step, rounds)
+    ms_step = st["median_ms"]
+    value = step.flops / (ms_step * 1e-3) / 1e12
+    log(f"timed region {args.steps} steps: {region_ms:.4f} ms/step; statistics over {rounds} "
+        f"steps: median {ms_step:.4f} min {st['min_ms']:.4f} mean {st['mean_ms']:.4f} "
+        f"sd {st['stddev_ms']:.4f} ms -> {value:.2f} TFLOP/s; sclk {clk.summary()}")
+    # Per-kernel durations: the library records a hipEvent pair around each kernel launch on
+    # the stream it launches on, over the same number of steps again.
     S.sdpa_profile_enable(True)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(rounds):
         step()
     torch.cuda.synchronize()
-    t3 = time.perf_counter()
     S.sdpa_profile_enable(False)
     kern = S.sdpa_profile_read()
-    prof_ms = (t3 - t2) * 1e3 / args.steps
-    log(f"per-kernel pass: {prof_ms:.4f} ms/step with per-launch events")
-    kernels = {name: {"launches": n, "avg_ms": tot / n} for name, (n, tot) in kern.items()}
+    kernels = {name: {"launches": n, "avg_ms": round(tot / n, 6)} for name, (n, tot) in kern.items()}
     dom = max(kern, key=lambda n: kern[n][1])
     dom_ms = kern[dom][1] / kern[dom][0]
-    if dom in alg_flops:
-        ach = alg_flops[dom] / (dom_ms * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3),
-                "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_TFLOPS["bf16"], 5),
-                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": round(dom_ms, 6),
-                "algorithmic_flops_per_launch": alg_flops[dom]}
-    else:
-        nbytes = 2 * w.batch * w.seqlen_q * w.heads_q * d * 2 + w.batch * w.heads_q * w.seqlen_q * 4
-        ach = nbytes / (dom_ms * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 5),
-                "traffic": traffic_for(dom, args.workload), "avg_launch_ms": round(dom_ms, 6)}
+    ach = step.alg_flops[dom] / (dom_ms * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(ach / peak, 5), "traffic": traffic_for(dom, wl),
+            "avg_launch_ms": round(dom_ms, 6),
+            "algorithmic_flops_per_launch": step.alg_flops[dom]}
+    log(f"kernels: {kernels}; roofline {dom}: {ach:.1f} TFLOP/s = {ach / peak:.4f} of {peak}")
 
+    cfg = {"workload": MFMA_WORKLOADS[wl], "dtype": dtype, "heads_q": w.heads_q,
+           "heads_kv": w.heads_kv, "head_dim": w.head_dim, "mask": "causal",
+           "softmax_scale": w.scale, "visible_pairs": step.nvis, "flops_per_step": step.flops}
+    if w.is_thd:
+        import numpy as np
+        cfg.update({"layout": "thd", "sequences": w.batch,
+                    "lengths": np.diff(w.cu_seqlens_q).astype(int).tolist(),
+                    "total_tokens": int(w.cu_seqlens_q[-1])})
+    else:
+        cfg.update({"layout": w.layout, "batch": w.batch, "seq_len": w.seqlen_q})
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": MFMA_WORKLOADS[args.workload],
-                   "batch": w.batch, "seq_len": w.seqlen_q, "heads": w.heads_q,
-                   "head_dim": w.head_dim, "mask": "causal", "flops_per_step": flops_step},
-        "frac_of_peak": round(value / PEAK_TFLOPS["bf16"], 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": cfg,
+        "frac_of_peak": round(value / peak, 5),
+        "step_stats": st,
+        "timed_region": {"steps": args.steps, "ms_per_step": round(region_ms, 5),
+                         "TFLOP/s": round(step.flops / (region_ms * 1e-3) / 1e12, 3)},
+        "sclk": clk.summary(),
         "roofline": roof,
         "kernels": kernels,
-        "kernel_timing": ("per-launch hipEvent pairs on the launch stream, in a second pass of "
-                          f"the same {args.steps} steps ({prof_ms:.4f} ms/step with the events)"),
+        "kernel_timing": ("per-launch hipEvent pairs recorded by the library on the launch "
+                          f"stream, over {rounds} further steps"),
     }
 
     if not args.no_extra:
         out["extra"] = extra(torch, S, synth, dev)
 
-    if not args.no_cpu and args.workload == "c2":
-        out["cpu_baseline"] = cpu_baseline(w, flops_step)
+    if not args.no_cpu and wl in ("c4", "c2"):
+        out["cpu_baseline"] = cpu_baseline(w, step)
 
     print(json.dumps(out), flush=True)
     return 0
 
 
 MFMA_WORKLOADS = {
+    "c4": ("varlen THD causal self-attention fwd+bwd, bf16: 8 sequences with lengths uniform on "
+           "[256,4096] (seed 0), int32 cu_seqlens, 16 q heads, 4 kv heads (GQA), head_dim 128, "
+           "scale 1/sqrt(128), N(0,1) q, k, v, dO"),
     "c2": ("causal self-attention fwd+bwd, bf16, B4 S1024 H8 D64, BSHD contiguous, scale 1/8, "
            "N(0,1) inputs"),
     "target": ("causal self-attention forward, bf16, B8 S4096 H8 D64, BSHD contiguous, scale 1/8, "
@@ -229,6 +347,8 @@ MFMA_WORKLOADS = {
                     "scale 1/sqrt(128), N(0,1) inputs"),
     "target_step": ("causal self-attention fwd+bwd, bf16, B8 S4096 H8 D64, BSHD contiguous, "
                     "scale 1/8, N(0,1) inputs"),
+    "f32_step": ("causal self-attention fwd+bwd, fp32, B4 S4096 H8 D64, BSHD contiguous, "
+                 "scale 1/8, N(0,1) inputs"),
 }
 
 HBM_WORKLOADS = {
@@ -329,14 +449,16 @@ def copy_calibration() -> int:
     return 0
 
 
-def time_calls(torch, fn, iters=10, warm=3):
+def time_calls(torch, fn, warm=3):
+    """Median of per-call hipEvent times over at least 20 calls and 50 ms (warm-up calls
+    discarded first)."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     with Timer(torch) as tm:
-        for _ in range(iters):
-            fn()
-    return tm.ms() / iters
+        fn()
+    est = tm.ms()
+    return step_stats(torch, fn, stat_rounds(est, lo=20, min_ms=50.0, hi=1000))["median_ms"]
 
 
 def extra(torch, S, synth, dev):
@@ -367,20 +489,11 @@ def extra(torch, S, synth, dev):
     res["c3_fwd_f16_packed"] = {"ms": round(ms, 4),
                                 "TFLOP/s": round(4 * 64 * nvis / (ms * 1e-3) / 1e12, 2)}
 
-    # varlen THD GQA bf16 fwd + bwd
-    w = synth.c4()
-    q, k, v, g = (t.to(dev) for t in (w.q, w.k, w.v, w.dout))
-    cu = torch.from_numpy(w.cu_seqlens_q).to(dev)
-    lens = [int(x) for x in (w.cu_seqlens_q[1:] - w.cu_seqlens_q[:-1])]
-    nvis = 16 * sum(L * (L + 1) // 2 for L in lens)
-    o, lse = S.forward(q, k, v, "thd", w.scale, (-1, 0), cu_seqlens_q=cu, max_seqlen_q=max(lens))
-    msf = time_calls(torch, lambda: S.forward(q, k, v, "thd", w.scale, (-1, 0), cu_seqlens_q=cu,
-                                              max_seqlen_q=max(lens), out=o, lse=lse))
-    msb = time_calls(torch, lambda: S.backward(q, k, v, o, lse, g, "thd", w.scale, (-1, 0),
-                                               cu_seqlens_q=cu, max_seqlen_q=max(lens)))
-    res["c4_thd_gqa_bf16"] = {"lengths": lens, "fwd_ms": round(msf, 4), "bwd_ms": round(msb, 4),
-                              "fwd_TFLOP/s": round(4 * 128 * nvis / (msf * 1e-3) / 1e12, 2),
-                              "bwd_TFLOP/s": round(10 * 128 * nvis / (msb * 1e-3) / 1e12, 2)}
+    # the pages' bf16 causal case (B4 S1024 H8 D64): latency-bound, reported for context
+    res["c2_causal_fwd_bwd_bf16"] = fwd_bwd_split(torch, S, synth.c2(), dev)
+    # fp32 (true fp32: scores in fp64, no reduced-precision products) against the fp32 peak
+    res["f32_causal_fwd_bwd"] = fwd_bwd_split(torch, S, synth.target(b=4, s=4096, with_grad=True,
+                                                                      dtype="f32"), dev)
 
     res["block_sparse_bf16"] = block_sparse(torch, S, synth, dev)
     res["fp8_e4m3_fwd"] = fp8_forward(torch, S, synth, dev)
@@ -421,13 +534,28 @@ def extra(torch, S, synth, dev):
                    "bwd_GB/s": round(bbytes / (msb * 1e-3) / 1e9, 1)})
         del q, k, v, o, lse, g, dq, dk, dv
     res["short_seq_fwd_bf16"] = ss
-    try:
-        clk = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
-                             timeout=20).stdout
-        res["sclk"] = [l.strip() for l in clk.splitlines() if "sclk" in l.lower()][:2]
-    except Exception:  # pragma: no cover
-        pass
     return res
+
+
+def fwd_bwd_split(torch, S, w, dev):
+    """Forward and backward of one workload timed separately (median per call), with
+    TFLOP/s and the fraction of the dtype's dense MFMA peak."""
+    fwd = Step(torch, S, w, dev, fwd_only=True)
+    both = Step(torch, S, w, dev)
+    msf = time_calls(torch, fwd)
+    msb = time_calls(torch, both) - msf
+    peak = PEAK_TFLOPS[w.dtype]
+    tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
+    d, n = w.head_dim, fwd.nvis
+    r = {"dtype": w.dtype, "B": w.batch, "S": w.seqlen_q, "Hq": w.heads_q, "Hk": w.heads_kv,
+         "D": d, "fwd_ms": round(msf, 4), "bwd_ms": round(msb, 4),
+         "fwd_TFLOP/s": round(tf(4 * d * n, msf), 2), "bwd_TFLOP/s": round(tf(10 * d * n, msb), 2),
+         "fwd_frac": round(tf(4 * d * n, msf) / peak, 4), "bwd_frac": round(tf(10 * d * n, msb) / peak, 4),
+         "peak_TFLOP/s": peak, "bwd_ms_is": "fwd+bwd step median minus fwd median"}
+    log(f"{w.name} {w.dtype} B{w.batch} S{w.seqlen_q} D{d}: fwd {msf:.3f} ms ({r['fwd_TFLOP/s']} TF), "
+        f"bwd {msb:.3f} ms ({r['bwd_TFLOP/s']} TF)")
+    del fwd, both
+    return r
 
 
 def block_sparse(torch, S, synth, dev):
@@ -513,33 +641,88 @@ def fp8_forward(torch, S, synth, dev):
     return out
 
 
-def cpu_baseline(w, flops_step):
-    """The fp64 oracle (as it stands) on the full step: forward then backward, every head."""
-    import numpy as np
-    import oracle
-    import synth
+def host_cores():
+    """Logical cores of the host, the cores this process may run on, the BLAS pool and the
+    CPU model."""
+    info = {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+    try:
+        info["nproc"] = int(subprocess.run(["nproc"], capture_output=True, text=True,
+                                           timeout=10).stdout.strip())
+    except Exception:  # pragma: no cover
+        info["nproc"] = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info["blas_threads"] = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        threads = 1
-    f = lambda t: synth.f64(synth.to_bhsd(t, w.layout))
-    q, k, v, g = (f(t) for t in (w.q, w.k, w.v, w.dout))
-    times = []
-    reps = 0
-    t_start = time.perf_counter()
-    while reps < 5 and (time.perf_counter() - t_start) < 20.0:
-        t0 = time.perf_counter()
-        oracle.windowed_forward(q, k, v, w.scale, w.window)
-        oracle.windowed_backward(q, k, v, g, w.scale, w.window)
-        times.append(time.perf_counter() - t0)
-        reps += 1
-    med = float(np.median(times))
-    log(f"oracle step {med:.3f} s over {reps} runs, {threads} threads")
-    return {"value": round(flops_step / med / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds_per_step": round(med, 4),
-            "sample": f"the full step (fp64 forward then backward of all 4x8 heads, "
-                      f"B4 S1024 D64 causal), median of {reps} runs"}
+        info["blas_threads"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f
+                                      if l.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        info["cpu_model"] = None
+    return info
+
+
+def cpu_baseline(w, step, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same step: forward then
+    backward of whole sequences (THD) or whole batch entries, every head, taken in a fixed
+    order until about ``budget_s`` seconds of CPU time have passed.  The rate is the sample's
+    algorithmic flops over its time; the full step's time is extrapolated by visible pairs."""
+    import numpy as np
+    import oracle
+    import scaled_dot_product_05_amd as S
+    import synth
+    cores = host_cores()
+    d, done_pairs, units = w.head_dim, 0, []
+    t0 = time.perf_counter()
+    if w.is_thd:
+        # units: (sequence, kv head with its group of q heads), in the workload's order
+        cu = w.cu_seqlens_q
+        grp = w.heads_q // w.heads_kv
+        for s_ in range(w.batch):
+            a, b = int(cu[s_]), int(cu[s_ + 1])
+            for kh in range(w.heads_kv):
+                hs = slice(kh * grp, (kh + 1) * grp)
+                sl = lambda t, h: synth.f64(t[a:b, h]).transpose(1, 0, 2)[None]
+                q, g = sl(w.q, hs), sl(w.dout, hs)
+                k, v = sl(w.k, slice(kh, kh + 1)), sl(w.v, slice(kh, kh + 1))
+                oracle.windowed_forward(q, k, v, w.scale, w.window)
+                oracle.windowed_backward(q, k, v, g, w.scale, w.window)
+                done_pairs += grp * S.n_visible(b - a, b - a, w.window)
+                units.append((s_, b - a, kh))
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    else:
+        f = lambda t: synth.f64(synth.to_bhsd(t, w.layout))
+        for bi in range(w.batch):
+            q, k, v, g = (f(t[bi:bi + 1]) for t in (w.q, w.k, w.v, w.dout))
+            oracle.windowed_forward(q, k, v, w.scale, w.window)
+            oracle.windowed_backward(q, k, v, g, w.scale, w.window)
+            done_pairs += w.heads_q * S.n_visible(w.seqlen_q, w.seqlen_k, w.window)
+            units.append((bi, w.seqlen_q, None))
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    per = {}
+    for u, L, kh in units:
+        per.setdefault((u, L), []).append(kh)
+    what = "; ".join((f"sequence {u} ({L} tokens), kv heads {hs[0]}-{hs[-1]} of {w.heads_kv}"
+                      if hs[0] is not None else f"batch entry {u}") for (u, L), hs in per.items())
+    fl = 14 * d * done_pairs
+    full_s = el * step.nvis / done_pairs
+    log(f"oracle: {len(units)} units, {el:.2f} s, {fl / el / 1e12:.6f} TFLOP/s; full step "
+        f"~{full_s:.1f} s; cores {cores}")
+    return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores["blas_threads"] or cores["affinity"], "kind": "oracle",
+            "sample": (f"fp64 oracle forward then backward of {what} "
+                       f"of the same workload: {done_pairs} of its {step.nvis} visible pairs, "
+                       f"one run, {el:.2f} s; value = those pairs' algorithmic flops "
+                       f"(14 D per pair) / time"),
+            "seconds": round(el, 3), "extrapolated_seconds_per_step": round(full_s, 2),
+            "host": cores}
 
 
 if __name__ == "__main__":

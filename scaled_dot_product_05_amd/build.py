@@ -26,9 +26,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, defines=(), tag: str = "") -> str:
-    obj = os.path.join(BUILD, tag + src + ".o")
-    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -39,13 +39,12 @@ def _compile(src: str, defines=(), tag: str = "") -> str:
     return obj
 
 
-def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
-    """Compile and link; ``defines`` (NAME=VALUE) select tile configurations."""
+def build(verbose: bool = True, out: str = LIB) -> str:
+    """Compile every source and link the library."""
     os.makedirs(BUILD, exist_ok=True)
-    tag = "" if not defines else "_".join(d.replace("=", "") for d in defines) + "."
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda src: _compile(src, defines, tag), SOURCES))
+        objs = list(ex.map(_compile, SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

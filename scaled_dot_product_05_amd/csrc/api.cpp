@@ -387,7 +387,7 @@ int device_cus() {
 // where the longest dK/dV chain (G times the longest dQ chain) sets the time.  On larger
 // grids the extra blocks and the partial sums cost more than the shorter chain saves.
 bool bwd_split_ok(const Shape& s, int32_t dtype) {
-  if (kBwdSplit == 0 || s.group < 2 || dtype == SDPA_DTYPE_F32 || dtype == SDPA_DTYPE_FP8_E4M3 ||
+  if (s.group < 2 || dtype == SDPA_DTYPE_F32 || dtype == SDPA_DTYPE_FP8_E4M3 ||
       (s.d != 64 && s.d != 128) || s.bm.bits)
     return false;
   const int64_t tk = kBwdK16, tq = kBwdQ16;

@@ -5,7 +5,10 @@
 // LSE is differentiated, so the backward receives dLSE):
 //   Delta_i = dO_i . O_i - dLSE_i,   P_ij = exp(s_ij - LSE_i),   dP = dO V^T,
 //   dS_ij = P_ij (dP_ij - Delta_i),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
-// Launches on one stream, no atomics anywhere:
+// Launches on one stream.  No gradient is ever accumulated with atomics: every element of
+// dQ, dK and dV has one writer.  The only atomic operation is an arrival counter of the
+// GQA dK/dV split (two workgroups per small-grid dK/dV block, see bwd_fused16p_kernel):
+// the half that arrives second adds the other's fp32 partial sums, in a fixed order.
 //   pre   Delta and LSE log2(e) for every query row (streaming, HBM bound);
 //   dq    one workgroup per 64 (16-bit) or 128 (fp32) query rows of a q head, streaming
 //         the key tiles;
@@ -103,7 +106,7 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
   if (bid < 0) bid = blockIdx.x;
   if (s.thd) {
     int item, h;
-    if (GROUPED && kBwdXcdOrder && heads % kXcds == 0) {
+    if (GROUPED && heads % kXcds == 0) {
       // XCD x (block b on XCD b % 8) runs the contiguous heads [x per, (x + 1) per), so a kv
       // group's q heads share an XCD (head_dim 128 kernels; C4's THD GQA backward
       // 1045 -> 988 us)
@@ -128,7 +131,7 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
   bool grouped = false;
   if constexpr (GROUPED) {
     const int hg = kBwdHeadGroup * (heads == s.hk ? 1 : s.group);
-    grouped = kBwdXcdOrder && bh % kXcds == 0 && !uniform && kBwdHeadGroup > 0 &&
+    grouped = bh % kXcds == 0 && !uniform &&
               (bh / kXcds) % hg == 0 && bh / kXcds > hg;
     if (grouped) {
       const int per = bh / kXcds, x = bid % kXcds, k = bid / kXcds;
@@ -139,7 +142,7 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
   }
   if (grouped) {
     // r and t set above
-  } else if (kBwdXcdOrder && bh % kXcds == 0 && (uniform || s.group > 1)) {
+  } else if (bh % kXcds == 0 && (uniform || s.group > 1)) {
     // Block b runs on XCD b % 8 (dQ blocks follow a multiple of 8 dK/dV blocks in the fused
     // launch).  XCD x owns the pairs [x per, (x + 1) per): for dK/dV the (batch, kv head)
     // pairs and for dQ the (batch, q head) pairs of the same kv heads, so a kv group's K/V
@@ -1864,7 +1867,7 @@ bool bwd_block_mask_ok(const BwdParams& p, DType dt) {
 // q, k, v, o, dO, dq, dk, dv 16-byte aligned.
 static bool bwd_short(const BwdParams& p, DType dt) {
   constexpr int need = kAlQ | kAlK | kAlV | kAlO | kAlDO | kAlDQ | kAlDK | kAlDV;
-  return kBwdShortRows > 0 && dt != DType::F32 && p.s.d <= 64 && p.s.sq <= kBwdShortRows &&
+  return dt != DType::F32 && p.s.d <= 64 && p.s.sq <= kBwdShortRows &&
          p.s.sk <= kBwdShortRows && !p.s.bm.bits && (p.aligned & need) == need;
 }
 

@@ -41,7 +41,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_til
   const Shape& s = p.s;
   if (s.thd) {
     int item, h;
-    if (kFwdXcdOrder && s.hq % kXcds == 0) {
+    if (s.hq % kXcds == 0) {
       // XCD x (block b on XCD b % 8) runs the contiguous q heads [x per, (x + 1) per), so
       // the q heads of one kv group share an XCD's L2
       const int per = s.hq / kXcds, j = blockIdx.x / kXcds;
@@ -63,19 +63,19 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int rows_per_til
   int t, r;
   // every q tile sees all sk keys (no window bound cuts any tile's range, no block mask)
   const bool uniform = s.uniform != 0;
-  if (kFwdXcdOrder && bh % kXcds == 0) {
+  if (bh % kXcds == 0) {
     // XCD x (block b runs on XCD b % 8) owns the (batch, head) pairs [x per, (x + 1) per),
     // so the q heads of one kv group share an XCD and its L2.  Tiles of equal cost: the XCD
     // walks its pairs one after the other, so the workgroups resident at one time cover a
     // few heads.  Otherwise (causal or window masks) its tiles go longest first across its
     // pairs, which balances the CUs better.
     const int per = bh / kXcds, x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-    if (!uniform && kFwdHeadGroup > 0 && per % kFwdHeadGroup == 0 && per > kFwdHeadGroup) {
+    if (!uniform && per % kFwdHeadGroup == 0 && per > kFwdHeadGroup) {
       // many pairs per XCD: groups of kFwdHeadGroup pairs one after the other, longest
       // tile first within a group (fewer heads' K/V resident than longest first over all
       // the XCD's pairs, with most of its balance; causal B8 S4096 D128 672 -> 638 us,
       // B16 S2048 D128 438 -> 404 us, D64 B8 S4096 201 -> 199 us)
-      constexpr int G = kFwdHeadGroup > 0 ? kFwdHeadGroup : 1;
+      constexpr int G = kFwdHeadGroup;
       const int gi = k / (G * nt), kk = k - gi * G * nt;
       r = x * per + gi * G + kk % G;
       t = kk / G;
@@ -1220,7 +1220,7 @@ bool fwd_block_mask_ok(const FwdParams& p, DType dt) { return dt == DType::F32 |
 // reads rows with 16-byte vector loads, so every row start must be 16-byte aligned.
 static bool fwd_short(const FwdParams& p) {
   constexpr int need = kAlQ | kAlK | kAlV | kAlO;
-  return kFwdShortRows > 0 && p.s.sq <= kFwdShortRows && !p.s.bm.bits && (p.aligned & need) == need;
+  return p.s.sq <= kFwdShortRows && !p.s.bm.bits && (p.aligned & need) == need;
 }
 
 template <bool BF, int D>
@@ -1243,15 +1243,6 @@ static hipError_t go16(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = fwd_grid(p, BM);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const int64_t kv_ss0 = p.k.ss > p.v.ss ? p.k.ss : p.v.ss;
-  const bool al0 = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
-  if constexpr (D == 64 && kFwdWideD64) {
-    // 64 query rows per wave when the grid still fills the chip twice over
-    const int64_t wide = fwd_grid(p, 2 * BM);
-    if (al0 && p.k.ss >= D && p.v.ss >= D && (int64_t(p.s.sk) + 4 * 32) * kv_ss0 * 2 < (int64_t(1) << 31) &&
-        !p.s.thd && !p.s.bm.bits && wide >= kFwdWideMinBlocks)
-      return go(fwd16p_kernel<BF, D, MINB, 2, 32, false>, int(wide), st, p);
-  }
   const bool al = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
   if (fwd_pipelined(p)) {
     if (p.s.bm.bits) return go(fwd16p_kernel<BF, D, MINB, 1, kFwdBNP, true>, int(blocks), st, p);
