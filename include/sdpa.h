@@ -269,6 +269,22 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
              const sdpa_tensor_t* dk, const sdpa_tensor_t* dv, int accumulate, void* workspace,
              size_t workspace_bytes, void* stream);
 
+/* sdpa_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the workspace
+ * taken from a static device buffer of sdpa_bwd_noalloc_max_workspace() bytes (64 MiB) that
+ * each GPU holds until the process ends, instead of the caller's.  Arguments, results and
+ * errors as sdpa_bwd; a problem whose sdpa_bwd_workspace_size exceeds the buffer returns
+ * ERR_WORKSPACE before anything runs.  Allocates nothing (no hipMalloc / hipFree).  Every
+ * call on one GPU shares that GPU's buffer: calls that overlap on one GPU (other streams or
+ * host threads) race and must be serialised by the caller; calls on one stream are ordered.
+ * The buffer needs no clearing: each call's kernels write what they later read. */
+size_t sdpa_bwd_noalloc_max_workspace(void);
+int sdpa_bwd_noalloc(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
+                     const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
+                     const sdpa_tensor_t* dout, const sdpa_rowstat_t* dlse,
+                     const sdpa_tensor_t* dq, const sdpa_tensor_t* dk, const sdpa_tensor_t* dv,
+                     int accumulate, void* stream);
+
 /* Builds the block table of `mask` (kv_count, kv_list, q_count, q_list) from its bits on
  * `stream`: every block of the (seqlen_q, seqlen_k) plane is classified over its pairs
  * inside the plane (the last block row and column may be short).  Asynchronous; reads only

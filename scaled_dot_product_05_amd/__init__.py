@@ -99,6 +99,9 @@ _SIGNATURES = {
     "sdpa_merge_bwd": ([_P(MergeDesc), _P(Tensor), _P(RowStat), _P(Tensor), _P(RowStat),
                         _P(Tensor), _P(RowStat), _P(Tensor), _P(RowStat), _P(Tensor),
                         _P(RowStat), ctypes.c_void_p], ctypes.c_int),
+    "sdpa_bwd_noalloc_max_workspace": ([], ctypes.c_size_t),
+    "sdpa_bwd_noalloc": ([_P(Desc)] + [_P(Tensor)] * 4 + [_P(RowStat), _P(Tensor), _P(RowStat)]
+                         + [_P(Tensor)] * 3 + [ctypes.c_int, ctypes.c_void_p], ctypes.c_int),
     "sdpa_block_mask_build": ([_P(BlockMaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p],
                               ctypes.c_int),
     "sdpa_cp_workspace_size": ([_P(Desc), ctypes.c_int, _P(ctypes.c_size_t)], ctypes.c_int),
@@ -285,6 +288,18 @@ def sdpa_bwd(desc, q, k, v, o, lse, dout, dlse, dq, dk, dv, accumulate: bool = F
     _check(lib().sdpa_bwd(ctypes.byref(desc), tensor(q), tensor(k), tensor(v), tensor(o),
                           rowstat(lse), tensor(dout), rowstat(dlse), tensor(dq), tensor(dk),
                           tensor(dv), int(bool(accumulate)), wp, wb, _stream(stream)))
+
+
+def sdpa_bwd_noalloc_max_workspace() -> int:
+    return lib().sdpa_bwd_noalloc_max_workspace()
+
+
+def sdpa_bwd_noalloc(desc, q, k, v, o, lse, dout, dlse, dq, dk, dv, accumulate: bool = False,
+                     stream=None) -> None:
+    """sdpa_bwd with the library's static scratch buffer as workspace (no allocation)."""
+    _check(lib().sdpa_bwd_noalloc(ctypes.byref(desc), tensor(q), tensor(k), tensor(v), tensor(o),
+                                  rowstat(lse), tensor(dout), rowstat(dlse), tensor(dq),
+                                  tensor(dk), tensor(dv), int(bool(accumulate)), _stream(stream)))
 
 
 def sdpa_merge_fwd_validate(mdesc, x_a, lse_a, x_b, lse_b, x, lse) -> None:

@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libsdpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "profile.cpp", "cp.cpp", "fwd.hip", "bwd.hip", "merge.hip", "sched.hip", "blockmask.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "cp.cpp", "fwd.hip", "bwd.hip", "merge.hip", "sched.hip", "blockmask.hip",
+           "noalloc.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]

@@ -20,13 +20,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "sdpa.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(sdpa_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(sdpa_\w+)\(", text, re.M)))
 
 
 def test_every_declared_symbol_is_exported_and_bound():
     lib = S.lib()
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.exported_symbols())
