@@ -151,8 +151,14 @@ int64_t floordiv(int64_t a, int64_t b) {
 // True when A and B provably share no address.  Either their byte ranges are apart, or
 // both are boxes of one non-overlapping parent with the same strides (e.g. disjoint head
 // ranges of a packed [s, b, h_total, d] buffer, or disjoint row ranges of one tensor).
-bool provably_disjoint(const Norm& a, const Norm& b) {
-  if (a.numel() == 0 || b.numel() == 0) return true;
+bool provably_disjoint(const Norm& a0, const Norm& b0) {
+  if (a0.numel() == 0 || b0.numel() == 0) return true;
+  // a dim of stride 0 (a broadcast input) addresses what extent 1 addresses
+  Norm a = a0, b = b0;
+  for (int i = 0; i < 4; ++i) {
+    if (a.st[i] == 0) a.n[i] = 1;
+    if (b.st[i] == 0) b.n[i] = 1;
+  }
   uintptr_t alo, ahi, blo, bhi;
   byte_span(a, &alo, &ahi);
   byte_span(b, &blo, &bhi);
@@ -173,25 +179,34 @@ bool provably_disjoint(const Norm& a, const Norm& b) {
   }
   if (m == 0) return false;  // two single elements at the same address
   std::sort(act, act + m, [&](int x, int y) { return st[x] > st[y]; });
-  int64_t c[4] = {0, 0, 0, 0};
-  int64_t rem = delta;
-  for (int k = 0; k < m; ++k) {
-    c[act[k]] = floordiv(rem, st[act[k]]);
-    rem -= c[act[k]] * st[act[k]];
-  }
-  if (rem != 0) return false;
-  // parent box and its injectivity (ascending strides, each above the span below it)
-  int64_t below = 0;
-  for (int k = m - 1; k >= 0; --k) {
-    int i = act[k];
-    int64_t lo = std::min<int64_t>(0, c[i]);
-    int64_t hi = std::max<int64_t>(a.n[i], c[i] + b.n[i]);
-    if (st[i] <= below) return false;
-    below += (hi - lo - 1) * st[i];
-  }
-  for (int k = 0; k < m; ++k) {
-    int i = act[k];
-    if (c[i] >= a.n[i] || c[i] + b.n[i] <= 0) return true;  // boxes apart along dim i
+  // B's origin sits at coordinates c relative to A's: delta = sum_i c_i st_i.  Taking the
+  // dims by decreasing stride, c_i is floor(rem / st_i) or one more (the smaller dims' part
+  // of delta may be negative, e.g. B at a later head but an earlier row).  Any candidate
+  // for which both boxes lie in one parent box whose addressing is injective (ascending
+  // strides, each above the span of the smaller ones) and which keeps the boxes apart along
+  // some dim is a proof: their elements sit at distinct coordinates of that box.
+  for (int pick = 0; pick < (1 << m); ++pick) {
+    int64_t c[4] = {0, 0, 0, 0};
+    int64_t rem = delta;
+    for (int k = 0; k < m; ++k) {
+      c[act[k]] = floordiv(rem, st[act[k]]) + ((pick >> k) & 1);
+      rem -= c[act[k]] * st[act[k]];
+    }
+    if (rem != 0) continue;
+    bool injective = true;
+    int64_t below = 0;
+    for (int k = m - 1; k >= 0 && injective; --k) {
+      int i = act[k];
+      int64_t lo = std::min<int64_t>(0, c[i]);
+      int64_t hi = std::max<int64_t>(a.n[i], c[i] + b.n[i]);
+      if (st[i] <= below) injective = false;
+      below += (hi - lo - 1) * st[i];
+    }
+    if (!injective) continue;
+    for (int k = 0; k < m; ++k) {
+      int i = act[k];
+      if (c[i] >= a.n[i] || c[i] + b.n[i] <= 0) return true;  // boxes apart along dim i
+    }
   }
   return false;
 }
@@ -252,6 +267,14 @@ int check_desc(const sdpa_desc_t* d, Shape* s) {
       return fail(SDPA_ERR_SHAPE, "total_q/total_k out of range");
   } else if (d->cu_seqlens_q_padded || d->cu_seqlens_k_padded) {
     return fail(SDPA_ERR_ARG, "cu_seqlens_*_padded are for the THD layout only");
+  }
+  {
+    // every element count and byte size derived from the shape stays far from int64
+    // overflow (workspace sizes and offsets are computed in int64)
+    const double rq = (thd ? double(d->total_q) : double(d->batch) * d->seqlen_q) * d->heads_q;
+    const double rk = (thd ? double(d->total_k) : double(d->batch) * d->seqlen_k) * d->heads_kv;
+    if (std::max(rq, rk) * double(d->head_dim) * 8.0 > 4.0e18)
+      return fail(SDPA_ERR_SHAPE, "problem too large: %.3g query rows, %.3g key rows", rq, rk);
   }
   const sdpa_block_mask_t* m = d->block_mask;
   if (m) {
