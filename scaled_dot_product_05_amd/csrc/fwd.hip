@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd16_kernel(FwdParams p) {
 // A block-sparse mask asks for one more workgroup per CU at head_dim <= 64 (its lists and
 // bits fit the LDS of three).
 template <bool BF, int D, int MINB, int QB, int BN, bool BSM>
-__global__ __launch_bounds__(kThreads, (BSM && D <= 64 && MINB < 3) ? 3 : MINB) void fwd16p_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, (D == 64 && MINB < 3) ? 3 : MINB) void fwd16p_kernel(FwdParams p) {
   constexpr int BM = 32 * QB * kWaves;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TB = BN * D * 2;          // bytes per K or V tile
