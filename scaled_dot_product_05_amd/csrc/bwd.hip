@@ -1019,15 +1019,32 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
   // S^T and dP^T of one tile: independent chains, interleaved
+  // At head_dim 128 (one wave per SIMD, registers to spare) every A operand of the tile is
+  // read before the first product, so the LDS latency is paid once per tile rather than
+  // before every pair of products.
   auto products = [&](int ks, int vs, f32x16_t& st, f32x16_t& dp) {
     st = zero16();
     dp = zero16();
+    if constexpr (D >= 128) {
+      uint4 a[NC], b2[NC];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const uint4 a = lds_read16(lds + ks * TB + ra[cc]);
-      const uint4 b2 = lds_read16(lds + (NSK + vs) * TB + ra[cc]);
-      st = mfma16<BF>(a, qf[cc], st);
-      dp = mfma16<BF>(b2, gf[cc], dp);
+      for (int cc = 0; cc < NC; ++cc) {
+        a[cc] = lds_read16(lds + ks * TB + ra[cc]);
+        b2[cc] = lds_read16(lds + (NSK + vs) * TB + ra[cc]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        st = mfma16<BF>(a[cc], qf[cc], st);
+        dp = mfma16<BF>(b2[cc], gf[cc], dp);
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const uint4 a = lds_read16(lds + ks * TB + ra[cc]);
+        const uint4 b2 = lds_read16(lds + (NSK + vs) * TB + ra[cc]);
+        st = mfma16<BF>(a, qf[cc], st);
+        dp = mfma16<BF>(b2, gf[cc], dp);
+      }
     }
   };
   // key j visible to query i iff lo_rel <= j - i - off <= min(hi_rel, sk - 1 - i - off)
@@ -1066,14 +1083,31 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
                            pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
   };
   auto dq_update = [&](int ks, const uint4(&dsf)[NPC]) {
+    if constexpr (D >= 128) {
+      uint2 lo[NPC][NDB], hi[NPC][NDB];
 #pragma unroll
-    for (int cc = 0; cc < NPC; ++cc)
+      for (int cc = 0; cc < NPC; ++cc)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const lds_t* base = lds + ks * TB + 16 * cc * CPR * 16;
-        const uint2 lo = read_tr16(base + ta[db][0]), hi = read_tr16(base + ta[db][1]);
-        acc[db] = mfma16<BF>(make_uint4(lo.x, lo.y, hi.x, hi.y), dsf[cc], acc[db]);
-      }
+        for (int db = 0; db < NDB; ++db) {
+          const lds_t* base = lds + ks * TB + 16 * cc * CPR * 16;
+          lo[cc][db] = read_tr16(base + ta[db][0]);
+          hi[cc][db] = read_tr16(base + ta[db][1]);
+        }
+#pragma unroll
+      for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma16<BF>(make_uint4(lo[cc][db].x, lo[cc][db].y, hi[cc][db].x, hi[cc][db].y), dsf[cc], acc[db]);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const lds_t* base = lds + ks * TB + 16 * cc * CPR * 16;
+          const uint2 lo = read_tr16(base + ta[db][0]), hi = read_tr16(base + ta[db][1]);
+          acc[db] = mfma16<BF>(make_uint4(lo.x, lo.y, hi.x, hi.y), dsf[cc], acc[db]);
+        }
+    }
   };
 
   const int n = BSM ? nbm * TPB : kt1 - kt0;
@@ -1328,16 +1362,31 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
 
   // S and dP of the tile in slot sl
+  // (head_dim 128: every A operand read before the first product, as in dQ)
   auto products = [&](int sl, f32x16_t& st, f32x16_t& dp) {
     const lds_t* base = lds + sl * SB;
     st = zero16();
     dp = zero16();
+    if constexpr (D >= 128) {
+      uint4 a[NC], b2[NC];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const uint4 a = lds_read16(base + ra[cc]);
-      const uint4 b2 = lds_read16(base + TB + ra[cc]);
-      st = mfma16<BF>(a, kf[cc], st);
-      dp = mfma16<BF>(b2, vf[cc], dp);
+      for (int cc = 0; cc < NC; ++cc) {
+        a[cc] = lds_read16(base + ra[cc]);
+        b2[cc] = lds_read16(base + TB + ra[cc]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        st = mfma16<BF>(a[cc], kf[cc], st);
+        dp = mfma16<BF>(b2[cc], vf[cc], dp);
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const uint4 a = lds_read16(base + ra[cc]);
+        const uint4 b2 = lds_read16(base + TB + ra[cc]);
+        st = mfma16<BF>(a, kf[cc], st);
+        dp = mfma16<BF>(b2, vf[cc], dp);
+      }
     }
   };
   // x = s c - LSE log2e and y = dP - Delta of item in slot sl: the first uses of its S and
@@ -1407,16 +1456,39 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       dsf[h2] = make_uint4(pack2<BF>(ds[8 * h2], ds[8 * h2 + 1]), pack2<BF>(ds[8 * h2 + 2], ds[8 * h2 + 3]),
                            pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
     }
+    if constexpr (D >= 128) {
+      uint2 g2[NPC][NDB][2], q2[NPC][NDB][2];
 #pragma unroll
-    for (int cc = 0; cc < NPC; ++cc)
+      for (int cc = 0; cc < NPC; ++cc)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const lds_t* rb = base + 16 * cc * CPR * 16;
-        const uint2 glo = read_tr16(rb + TB + ta[db][0]), ghi = read_tr16(rb + TB + ta[db][1]);
-        adv[db] = mfma16<BF>(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pf[cc], adv[db]);
-        const uint2 qlo = read_tr16(rb + ta[db][0]), qhi = read_tr16(rb + ta[db][1]);
-        adk[db] = mfma16<BF>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsf[cc], adk[db]);
-      }
+        for (int db = 0; db < NDB; ++db) {
+          const lds_t* rb = base + 16 * cc * CPR * 16;
+          g2[cc][db][0] = read_tr16(rb + TB + ta[db][0]);
+          g2[cc][db][1] = read_tr16(rb + TB + ta[db][1]);
+          q2[cc][db][0] = read_tr16(rb + ta[db][0]);
+          q2[cc][db][1] = read_tr16(rb + ta[db][1]);
+        }
+#pragma unroll
+      for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          adv[db] = mfma16<BF>(make_uint4(g2[cc][db][0].x, g2[cc][db][0].y, g2[cc][db][1].x, g2[cc][db][1].y),
+                               pf[cc], adv[db]);
+          adk[db] = mfma16<BF>(make_uint4(q2[cc][db][0].x, q2[cc][db][0].y, q2[cc][db][1].x, q2[cc][db][1].y),
+                               dsf[cc], adk[db]);
+        }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < NPC; ++cc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const lds_t* rb = base + 16 * cc * CPR * 16;
+          const uint2 glo = read_tr16(rb + TB + ta[db][0]), ghi = read_tr16(rb + TB + ta[db][1]);
+          adv[db] = mfma16<BF>(make_uint4(glo.x, glo.y, ghi.x, ghi.y), pf[cc], adv[db]);
+          const uint2 qlo = read_tr16(rb + ta[db][0]), qhi = read_tr16(rb + ta[db][1]);
+          adk[db] = mfma16<BF>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), dsf[cc], adk[db]);
+        }
+    }
   };
 
   // Step it reads item it (slot it % 4) and item it+1 (the next S and dP, issued before
