@@ -1131,25 +1131,31 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   // copies (measured: D64 B8 S4096 backward 568 -> 548 us, D128 B4 S4096 1180 -> 1273 us).
   f32x16_t sa, da, sb, db_;
   if (n > 0) products(0, 0, sa, da);
-  for (int i = 0; i < n; ++i) {
+  // one step: tile i's S and dP are in (cs, cd); the next tile's products go to (ns, nd)
+  auto step = [&](int i, f32x16_t& cs, f32x16_t& cd, f32x16_t& ns, f32x16_t& nd) {
     const int ph = i & 3;
     issue_k(tile_at(i + 3), (ph + 3) & 3, i + 3 < n && partial_at(i + 3));
     issue_v(tile_at(i + 3), (ph + 3) & 3);
     float x[16], y[16];
     if constexpr (D <= 64) {
-      consume(sa, da, x, y);
+      consume(cs, cd, x, y);
       __builtin_amdgcn_sched_barrier(0);
-      products((ph + 1) & 3, (ph + 1) & 3, sa, da);  // past the last tile: unused
+      products((ph + 1) & 3, (ph + 1) & 3, ns, nd);  // past the last tile: unused
     } else {
-      products((ph + 1) & 3, (ph + 1) & 3, sb, db_);
-      consume(sa, da, x, y);
+      products((ph + 1) & 3, (ph + 1) & 3, ns, nd);
+      consume(cs, cd, x, y);
     }
     uint4 dsf[NPC];
     grad(tile_at(i), partial_at(i), ph, x, y, dsf);
     dq_update(ph, dsf);
     vm_wait<2 * NDMA + NB>();
     lds_barrier();
-    if constexpr (D > 64) {
+  };
+  for (int i = 0; i < n; ++i) {
+    if constexpr (D <= 64) {
+      step(i, sa, da, sa, da);
+    } else {
+      step(i, sa, da, sb, db_);
       sa = sb;
       da = db_;
     }
@@ -1317,11 +1323,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
   // wave 0 loads the tile rows' LSE log2e, wave 1 their Delta (lanes 0..31)
   const i32x4_t rstat = make_rsrc(wave == 0 ? p.lse2 : p.delta, p.ws_rows * 4);
-  auto issue = [&](int it, int slot) {
-    it = min(it, n - 1);  // past the last item: reload it (never read), keeps wait counts fixed
-    int gi, qt;
-    bool part;
-    item(it, gi, qt, part);
+  auto issue_at = [&](int gi, int qt, bool part, int slot) {
     const int h = hk * s.group + gi, qbase = qt * BQ;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q.ptr) + w.b * p.q.sb + h * p.q.sh + g.qrow0 * qss;
     const uint16_t* gh = static_cast<const uint16_t*>(p.dout.ptr) + w.b * p.dout.sb + h * p.dout.sh +
@@ -1342,6 +1344,13 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       const uint32_t o = part ? uint32_t((qbase + l32) * s.bm.words * 8 + (kw0 / 32) * 4) : 0x80000000u;
       if (lane < 32) dma4(rb, (lds_t*)(bm_bits + slot * 64 + wave * 32), o);
     }
+  };
+  auto issue = [&](int it, int slot) {
+    it = min(it, n - 1);  // past the last item: reload it (never read), keeps wait counts fixed
+    int gi, qt;
+    bool part;
+    item(it, gi, qt, part);
+    issue_at(gi, qt, part, slot);
   };
 
   int ra[NC];
@@ -1407,12 +1416,9 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       }
     }
   };
-  // P, dS and the dV, dK updates of item `it` (slot sl), given consume's x and y
-  auto update = [&](int sl, int it, const float(&x)[16], const float(&y)[16]) {
+  // P, dS and the dV, dK updates of the item of tile qt (slot sl), given consume's x and y
+  auto update_at = [&](int sl, int qt, bool part, const float(&x)[16], const float(&y)[16]) {
     const lds_t* base = lds + sl * SB;
-    int gi, qt;
-    bool part;
-    item(it, gi, qt, part);
     const int qbase = qt * BQ;
     float pr[16], ds[16];
 #pragma unroll
@@ -1491,6 +1497,21 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     }
   };
 
+  auto update = [&](int sl, int it, const float(&x)[16], const float(&y)[16]) {
+    int gi, qt;
+    bool part;
+    item(it, gi, qt, part);
+    update_at(sl, qt, part, x, y);
+  };
+  // Without a block mask, items go head after head, tile after tile: a cursor (q head gi,
+  // q tile qt) steps to the next item with an increment, not a division by the tile count
+  auto advance = [&](int& gi, int& qt) {
+    if (++qt == qt1) {
+      qt = qt0;
+      ++gi;
+    }
+  };
+
   // Step it reads item it (slot it % 4) and item it+1 (the next S and dP, issued before
   // this item's softmax so the matrix cores run while the VALU works), loads item it+3 and
   // before its barrier waits for every load but its own, so item it+2 has landed.  At
@@ -1506,22 +1527,45 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     lds_barrier();
     products(0, sa, da);
   }
-  for (int it = 0; it < n; ++it) {
+  // cursors of item it and of item min(it + 3, n - 1), the one the step loads
+  int gi_c = 0, qt_c = 0, gi_a = 0, qt_a = 0;
+  bool pt_a = false;
+  if (!BSM && n > 0) {
+    item(0, gi_c, qt_c, pt_a);
+    item(min(3, n - 1), gi_a, qt_a, pt_a);
+  }
+  // one step: item it's S and dP are in (cs, cd); the next item's products go to (ns, nd)
+  auto step = [&](int it, f32x16_t& cs, f32x16_t& cd, f32x16_t& ns, f32x16_t& nd) {
     const int ph = it & (NS - 1);
-    issue(it + 3, (ph + 3) & (NS - 1));
+    if constexpr (BSM) {
+      issue(it + 3, (ph + 3) & (NS - 1));
+    } else {
+      issue_at(gi_a, qt_a, false, (ph + 3) & (NS - 1));
+      if (it + 3 < n - 1) advance(gi_a, qt_a);
+    }
     float x[16], y[16];
     if constexpr (D <= 64) {
-      consume(ph, sa, da, x, y);
+      consume(ph, cs, cd, x, y);
       __builtin_amdgcn_sched_barrier(0);
-      products((ph + 1) & (NS - 1), sa, da);  // past the last item: a reloaded tile, unused
+      products((ph + 1) & (NS - 1), ns, nd);  // past the last item: a reloaded tile, unused
     } else {
-      products((ph + 1) & (NS - 1), sb, db_);
-      consume(ph, sa, da, x, y);
+      products((ph + 1) & (NS - 1), ns, nd);
+      consume(ph, cs, cd, x, y);
     }
-    update(ph, it, x, y);
+    if constexpr (BSM) {
+      update(ph, it, x, y);
+    } else {
+      update_at(ph, qt_c, false, x, y);
+      advance(gi_c, qt_c);
+    }
     vm_wait<NL>();
     lds_barrier();
-    if constexpr (D > 64) {
+  };
+  for (int it = 0; it < n; ++it) {
+    if constexpr (D <= 64) {
+      step(it, sa, da, sa, da);
+    } else {
+      step(it, sa, da, sb, db_);
       sa = sb;
       da = db_;
     }
