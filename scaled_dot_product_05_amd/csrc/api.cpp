@@ -875,8 +875,7 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     sk.tile_own = bwd_k_rows(a.dtype);
     sk.tile_other = f32 ? 32 : kBwdKInner;
     sk.max_items = int32_t(thd_items(a.s.total_k, a.s.batch, sk.tile_own));
-    if ((e = launch_schedule(sq, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
-    if ((e = launch_schedule(sk, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
+    if ((e = launch_schedule2(sq, sk, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
     p.work_q = sq.items;
     p.count_q = sq.count;
     p.work_k = sk.items;

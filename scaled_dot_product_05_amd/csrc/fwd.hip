@@ -533,6 +533,25 @@ __global__ __launch_bounds__(kThreads, (D == 64 && MINB < 3) ? 3 : MINB) void fw
     for (int j = 0; j < QB; ++j)
 #pragma unroll
       for (int k2 = 0; k2 < NKB; ++k2) st[j][k2] = zero16();
+    if constexpr (D >= 128) {
+      // head_dim 128: the tile's 16 A operands are read four products ahead of their use
+      // (the compiler otherwise read each just before its product and waited for it; four
+      // more registers per slot fit the two-wave budget: 564 -> 554 us at B8 S4096 H16, a
+      // full prefetch at one wave per SIMD took 741 us)
+      constexpr int NA = NC * NKB, PF = 4;
+      uint4 a[NA];
+#pragma unroll
+      for (int u = 0; u < PF && u < NA; ++u)
+        a[u] = lds_read16(lds + b * TB + (u % NKB) * 32 * CPR * 16 + ka[u / NKB]);
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        if (u + PF < NA)
+          a[u + PF] = lds_read16(lds + b * TB + ((u + PF) % NKB) * 32 * CPR * 16 + ka[(u + PF) / NKB]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+          st[j][u % NKB] = mfma16<BF>(a[u], qf[j][u / NKB], st[j][u % NKB]);
+      }
+    } else {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
@@ -541,6 +560,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && MINB < 3) ? 3 : MINB) void fw
 #pragma unroll
         for (int j = 0; j < QB; ++j) st[j][k2] = mfma16<BF>(a, qf[j][cc], st[j][k2]);
       }
+    }
   };
   auto pv = [&](auto B, const uint4(&pf)[QB][NPC]) {
     constexpr int b = decltype(B)::value;

@@ -7,6 +7,8 @@
 namespace sdpa {
 
 hipError_t launch_schedule(const SchedParams& p, hipStream_t stream);
+// two lists in one launch (one workgroup each)
+hipError_t launch_schedule2(const SchedParams& a, const SchedParams& b, hipStream_t stream);
 // Context parallelism over THD: per chunk c of 2 cp, the per-sequence row starts and the
 // prefix of chunk lengths (out: int32 [2 cp][2][batch + 1]: starts, then prefix).
 hipError_t launch_cp_chunks(const int32_t* cu, const int32_t* padded, int32_t batch, int64_t total,

@@ -51,7 +51,13 @@ __device__ __forceinline__ int item_cost(const SchedParams& p, const SeqLens& L,
   return int(min<int64_t>(c, kSchedBuckets - 1));
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) {
+// Workgroup b builds list b (the backward's query-tile and key-tile lists in one launch).
+struct SchedPair {
+  SchedParams p[2];
+};
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedPair pp) {
+  const SchedParams& p = pp.p[blockIdx.x];
   __shared__ int hist[kSchedBuckets];
   __shared__ int part[kSchedThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -104,7 +110,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedParams p) 
 
 hipError_t launch_schedule(const SchedParams& p, hipStream_t st) {
   prof_begin(st, "thd_schedule");
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, p);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, SchedPair{{p, p}});
+  prof_end(st);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule2(const SchedParams& a, const SchedParams& b, hipStream_t st) {
+  prof_begin(st, "thd_schedule");
+  hipLaunchKernelGGL(schedule_kernel, dim3(2), dim3(kSchedThreads), 0, st, SchedPair{{a, b}});
   prof_end(st);
   return hipGetLastError();
 }

@@ -10,6 +10,9 @@
 namespace sdpa {
 
 hipError_t launch_schedule(const SchedParams&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_schedule2(const SchedParams&, const SchedParams&, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_cp_chunks(const int32_t*, const int32_t*, int32_t, int64_t, int32_t, int32_t*,
                             hipStream_t) {
   return hipErrorNotSupported;
