@@ -867,7 +867,7 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     SchedParams sq = sched_params(a.s, true, reinterpret_cast<WorkItem*>(ws + w.wq_off),
                                   reinterpret_cast<int32_t*>(ws + w.cq_off));
     const bool f32 = a.dtype == SDPA_DTYPE_F32;
-    sq.tile_own = bwd_q_rows(a.dtype);
+    sq.tile_own = bwd_q_tile_rows(p, DType(a.dtype));  // never more items than the workspace holds
     sq.tile_other = f32 ? 32 : kBwdQInner;
     sq.max_items = int32_t(thd_items(a.s.total_q, a.s.batch, sq.tile_own));
     SchedParams sk = sched_params(a.s, false, reinterpret_cast<WorkItem*>(ws + w.wk_off),

@@ -1019,13 +1019,15 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
   // S^T and dP^T of one tile: independent chains, interleaved
-  // At head_dim 128 (one wave per SIMD, registers to spare) every A operand of the tile is
-  // read before the first product, so the LDS latency is paid once per tile rather than
-  // before every pair of products.
+  // At head_dim 128 with two waves (one wave per SIMD, registers to spare) every A operand
+  // of the tile is read before the first product, so the LDS latency is paid once per tile
+  // rather than before every pair of products; with four waves the other wave of the SIMD
+  // hides it.
+  constexpr bool kPrefetch = D >= 128 && W == 2;
   auto products = [&](int ks, int vs, f32x16_t& st, f32x16_t& dp) {
     st = zero16();
     dp = zero16();
-    if constexpr (D >= 128) {
+    if constexpr (kPrefetch) {
       uint4 a[NC], b2[NC];
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
@@ -1083,7 +1085,7 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
                            pack2<BF>(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack2<BF>(ds[8 * h2 + 6], ds[8 * h2 + 7]));
   };
   auto dq_update = [&](int ks, const uint4(&dsf)[NPC]) {
-    if constexpr (D >= 128) {
+    if constexpr (kPrefetch) {
       uint2 lo[NPC][NDB], hi[NPC][NDB];
 #pragma unroll
       for (int cc = 0; cc < NPC; ++cc)
@@ -1249,6 +1251,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     }
     __syncthreads();
   }
+  const int n_all = n;  // items of the whole block (before a split)
   // a split block takes the first or the second half of the items
   int ib = 0;
   if constexpr (SPLIT) {
@@ -1264,22 +1267,29 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   auto item = [&](int it, int& gi, int& qt, bool& part) {
     if constexpr (SPLIT) it += ib;
     if constexpr (BSM) {
+      // the same order as without a mask: last listed tile first; one shared list: every q
+      // head at one tile before the next, per-head lists: head after head (last head first)
       int e, r;
       if (s.bm.nh == 1) {
-        gi = it / nper;
-        r = it - gi * nper;
+        gi = it % s.group;
+        r = nper - 1 - it / s.group;
         e = __builtin_amdgcn_readfirstlane(bm_list[r / TPQ]);
       } else {
-        const int v = __builtin_amdgcn_readfirstlane(bm_list[it / TPQ]);
+        r = n_all - 1 - it;
+        const int v = __builtin_amdgcn_readfirstlane(bm_list[r / TPQ]);
         gi = v >> 16;
         e = v & 0xffff;
-        r = it;
       }
       qt = min(max(e >> 1, 0), s.bm.nqb - 1) * TPQ + r % TPQ;
       part = (e & 1) != 0;
     } else {
-      gi = it / nq;
-      qt = qt0 + it % nq;
+      // last query tile first, every q head of the group at one tile before the next: the
+      // dK/dV blocks of a (sequence, kv head) that run at one time read the same Q and dO
+      // rows at about the same time, so the repeats hit in L2 (C4's backward: 2.77 -> 1.76
+      // GB read from beyond L2 per launch; ascending tiles head after head let the blocks
+      // drift apart by one tile per block)
+      gi = it % s.group;
+      qt = qt1 - 1 - it / s.group;
       part = false;
     }
   };
@@ -1503,12 +1513,12 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     item(it, gi, qt, part);
     update_at(sl, qt, part, x, y);
   };
-  // Without a block mask, items go head after head, tile after tile: a cursor (q head gi,
-  // q tile qt) steps to the next item with an increment, not a division by the tile count
+  // Without a block mask a cursor (q head gi, q tile qt) steps to the next item with an
+  // increment, not a division by the group size
   auto advance = [&](int& gi, int& qt) {
-    if (++qt == qt1) {
-      qt = qt0;
-      ++gi;
+    if (++gi == s.group) {
+      gi = 0;
+      --qt;
     }
   };
 
@@ -1617,9 +1627,11 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
 }
 
-// Second launch bound: waves per SIMD that registers and LDS allow (at D128: one).
+// Second launch bound: waves per SIMD that registers and LDS allow.  D128 dQ with four waves
+// (128 query rows sharing one K/V ring): 240 registers and two 64 KB workgroups per CU, so
+// two waves per SIMD; with two waves (64 rows) the LDS allows one.
 template <bool BF, int D, int W>
-__global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dq16p_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * W, (D == 128 && W == 2) ? 1 : 2) void bwd_dq16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DqP<D, W>::LDS];
   dq16p_body<BF, D, W, false>(p, (lds_t*)smem_, blockIdx.x);
 }
@@ -1904,6 +1916,24 @@ static bool pipelined_ok(const BwdParams& p, int64_t rows, int64_t ss_a, int64_t
          (rows + 4 * 64) * ss * 2 < (int64_t(1) << 31);
 }
 
+// head_dim 128, 16-bit, both pipelined kernels usable, no block mask and no dK/dV split:
+// dK/dV and dQ run as two launches, dQ with four waves per 128-row tile (two waves per SIMD;
+// in the fused launch both halves run at the dK/dV kernel's one wave per SIMD).  Measured:
+// B8 S4096 H16/4 backward 2180 -> 2010 us, H16/16 2175 -> 2040 us; varlen THD GQA (C4) 802
+// -> 811 us of kernels but a 0.5% shorter step (the fused launch filled the tail of the
+// longest dK/dV chain with dQ blocks).  Splitting the long dK/dV blocks into halves in the
+// separate launch took 495 -> 871 us (each half's release of its partial sums).
+static bool dq_wide(const BwdParams& p, DType dt) {
+  return dt != DType::F32 && p.s.d == 128 && !p.s.bm.bits && p.nsplit != 2 &&
+         pipelined_ok<128>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV) &&
+         pipelined_ok<128>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
+}
+
+int bwd_q_tile_rows(const BwdParams& p, DType dt) {
+  if (dt == DType::F32) return kBwdQ32;
+  return dq_wide(p, dt) ? kBwdQ16Wide : kBwdQ16;
+}
+
 template <int ES, bool BF>
 static hipError_t pre(const BwdParams& p, hipStream_t st) {
   const Shape& s = p.s;
@@ -1924,6 +1954,13 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
     static_assert(kBwdQ16 == 64 && kBwdK16 == 64, "tile rows of the pipelined kernels");
     const bool kv = pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV);
     const bool q = pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
+    if constexpr (D == 128) {
+      if (dq_wide(p, BF ? DType::BF16 : DType::F16)) {
+        hipError_t e = go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128);
+        if (e != hipSuccess) return e;
+        return go(bwd_dq16p_kernel<BF, D, 4>, "bwd_dq", bq, st, p, 256);
+      }
+    }
     if (kv && q) {
       if (bk + bq <= 0) return hipSuccess;
       const bool split = !p.s.bm.bits && p.nsplit == 2 && bk == p.split_blocks;
@@ -2007,7 +2044,7 @@ hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
   hipError_t e = dt == DType::F32 ? pre<4, false>(p, st)
                                    : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
   if (e != hipSuccess) return e;
-  const int tq = dt == DType::F32 ? kBwdQ32 : kBwdQ16, tk = dt == DType::F32 ? kBwdK32 : kBwdK16;
+  const int tq = bwd_q_tile_rows(p, dt), tk = dt == DType::F32 ? kBwdK32 : kBwdK16;
   int64_t bq = s.thd ? ((s.total_q + tq - 1) / tq + s.batch) * s.hq : int64_t((s.sq + tq - 1) / tq) * s.batch * s.hq;
   int64_t bk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk : int64_t((s.sk + tk - 1) / tk) * s.batch * s.hk;
   switch (dt) {

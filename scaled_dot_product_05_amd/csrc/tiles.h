@@ -31,6 +31,8 @@ constexpr int kFwdShortMinB = 3;  // its workgroups per CU, head_dim <= 64
 // in kBwdQInner tiles (16-bit) or 32-key tiles (fp32)
 constexpr int kBwdQ16 = 64;
 constexpr int kBwdQ32 = 128;
+// dQ rows per tile of the separate four-wave head_dim-128 dQ launch
+constexpr int kBwdQ16Wide = 128;
 constexpr int kBwdQInner = 64;
 // backward dK/dV: one workgroup owns kBwdK16 / kBwdK32 keys of one (batch, kv head); query
 // rows of every head of the group stream in kBwdKInner tiles (16-bit) or 32-row tiles (fp32)
