@@ -72,11 +72,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
       dot = __uint_as_float(ov.x) * __uint_as_float(gv.x) + __uint_as_float(ov.y) * __uint_as_float(gv.y) +
             __uint_as_float(ov.z) * __uint_as_float(gv.z) + __uint_as_float(ov.w) * __uint_as_float(gv.w);
     } else {
+      // one fma chain per 8-element chunk (the four-wave dQ kernel repeats these roundings)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        dot += to_f32<BF>(uint16_t(elem16(ov, e))) * to_f32<BF>(uint16_t(elem16(gv, e)));
+        dot = __builtin_fmaf(to_f32<BF>(uint16_t(elem16(ov, e))), to_f32<BF>(uint16_t(elem16(gv, e))), dot);
     }
   }
+  // butterfly over the row's TPR chunks
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
   if (live && c == 0) {
@@ -875,7 +877,9 @@ struct DqP {
   static constexpr int LDS = (NSK + NSV) * TB;
 };
 
-template <bool BF, int D, int W, bool BSM>
+// DELTA: the block also forms Delta_i = dO_i . O_i - dLSE_i and LSE_i log2(e) of its rows and
+// stores them for the dK/dV launch that follows (in place of the pre-pass)
+template <bool BF, int D, int W, bool BSM, bool DELTA = false>
 __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds, int bid) {
   constexpr int BM = 32 * W, BN = DqP<D, W>::BN, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DqP<D, W>::TB, NDMA = BN * CPR / NT;
@@ -959,7 +963,37 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
       qf[cc] = make_uint4(t.x ^ qsign, t.y ^ qsign, t.z ^ qsign, t.w ^ qsign);
       gf[cc] = *reinterpret_cast<const uint4*>(gb + qr * p.dout.ss + 16 * cc + 8 * hf);
     }
-    if (qi < g.sq) {
+    if constexpr (DELTA) {
+      // The same value as the pre-pass, bit for bit: one fma chain per 8-element chunk, then
+      // its butterfly over the row's 16 chunks.  This lane holds chunks c = 2 cc + hf, so the
+      // partners c^8, c^4, c^2 are chunks cc^4, cc^2, cc^1 of this lane and c^1 is the same
+      // chunk of lane l^32.
+      static_assert(NC == 8, "the butterfly below is the pre-pass's at head_dim 128");
+      const uint16_t* ob = static_cast<const uint16_t*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
+      float pc[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const uint4 ov = *reinterpret_cast<const uint4*>(ob + qr * p.o.ss + 16 * cc + 8 * hf);
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          d = __builtin_fmaf(to_f32<BF>(uint16_t(elem16(ov, e))), to_f32<BF>(uint16_t(elem16(gf[cc], e))), d);
+        pc[cc] = d;
+      }
+      float dot = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
+      dot += __shfl_xor(dot, 32);
+      if (qi < g.sq) {
+        const float l = p.lse.ptr[w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss];
+        lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+        const float dlse = p.dlse.ptr ? p.dlse.ptr[w.b * p.dlse.sb + w.h * p.dlse.sh + (g.qrow0 + qi) * p.dlse.ss] : 0.f;
+        dl = dot - dlse;
+        if (hf == 0) {
+          const int64_t r = delta_index(s, w.b, w.h, g, qi);
+          p.delta[r] = dl;
+          p.lse2[r] = lse2;
+        }
+      }
+    } else if (qi < g.sq) {
       const float l = p.lse.ptr[w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss];
       lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
       dl = p.delta[delta_index(s, w.b, w.h, g, qi)];
@@ -1630,10 +1664,10 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
 // Second launch bound: waves per SIMD that registers and LDS allow.  D128 dQ with four waves
 // (128 query rows sharing one K/V ring): 240 registers and two 64 KB workgroups per CU, so
 // two waves per SIMD; with two waves (64 rows) the LDS allows one.
-template <bool BF, int D, int W>
+template <bool BF, int D, int W, bool DELTA = false>
 __global__ __launch_bounds__(64 * W, (D == 128 && W == 2) ? 1 : 2) void bwd_dq16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DqP<D, W>::LDS];
-  dq16p_body<BF, D, W, false>(p, (lds_t*)smem_, blockIdx.x);
+  dq16p_body<BF, D, W, false, DELTA>(p, (lds_t*)smem_, blockIdx.x);
 }
 
 template <bool BF, int D, int W>
@@ -1926,7 +1960,8 @@ static bool pipelined_ok(const BwdParams& p, int64_t rows, int64_t ss_a, int64_t
 static bool dq_wide(const BwdParams& p, DType dt) {
   return dt != DType::F32 && p.s.d == 128 && !p.s.bm.bits && p.nsplit != 2 &&
          pipelined_ok<128>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV) &&
-         pipelined_ok<128>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
+         pipelined_ok<128>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ) &&
+         (p.aligned & kAlO) && p.o.ss >= 128;
 }
 
 int bwd_q_tile_rows(const BwdParams& p, DType dt) {
@@ -1956,9 +1991,10 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
     const bool q = pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
     if constexpr (D == 128) {
       if (dq_wide(p, BF ? DType::BF16 : DType::F16)) {
-        hipError_t e = go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128);
+        // dQ first: its blocks form Delta and LSE log2(e) of their rows for dK/dV (no pre-pass)
+        hipError_t e = go(bwd_dq16p_kernel<BF, D, 4, true>, "bwd_dq", bq, st, p, 256);
         if (e != hipSuccess) return e;
-        return go(bwd_dq16p_kernel<BF, D, 4>, "bwd_dq", bq, st, p, 256);
+        return go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128);
       }
     }
     if (kv && q) {
@@ -2041,9 +2077,11 @@ static hipError_t go_bwd_short(const BwdParams& p, hipStream_t st) {
 hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
   const Shape& s = p.s;
   if (bwd_short(p, dt)) return dt == DType::BF16 ? go_bwd_short<true>(p, st) : go_bwd_short<false>(p, st);
-  hipError_t e = dt == DType::F32 ? pre<4, false>(p, st)
-                                   : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
-  if (e != hipSuccess) return e;
+  if (!dq_wide(p, dt)) {
+    hipError_t e = dt == DType::F32 ? pre<4, false>(p, st)
+                                     : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
+    if (e != hipSuccess) return e;
+  }
   const int tq = bwd_q_tile_rows(p, dt), tk = dt == DType::F32 ? kBwdK32 : kBwdK16;
   int64_t bq = s.thd ? ((s.total_q + tq - 1) / tq + s.batch) * s.hq : int64_t((s.sq + tq - 1) / tq) * s.batch * s.hq;
   int64_t bk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk : int64_t((s.sk + tk - 1) / tk) * s.batch * s.hk;
