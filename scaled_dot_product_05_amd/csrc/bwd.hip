@@ -1165,8 +1165,33 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   // register copies carry them over.  head_dim 128 (one wave per SIMD) gains more from the
   // compiler interleaving the next products with the whole softmax, at the price of the
   // copies (measured: D64 B8 S4096 backward 568 -> 548 us, D128 B4 S4096 1180 -> 1273 us).
+  // This wave's own tiles [ia, ib): those with a key visible to one of its rows.  The block
+  // walks the keys of all its rows, so below the causal diagonal a wave's last tiles, and
+  // past the sequence end all of a wave's tiles, are masked for it; it skips their products,
+  // exponentials and dQ update and only issues loads and meets the barriers.
+  int ia = 0, ib = n;
+  if constexpr (!BSM) {
+    int wj0 = 0, wj1 = 0;
+    if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+    if (wj1 > wj0) {
+      ia = min(max(wj0 / BN - kt0, 0), n);
+      ib = min(max((wj1 + BN - 1) / BN - kt0, ia), n);
+    } else {
+      ia = ib = 0;
+    }
+    ia = __builtin_amdgcn_readfirstlane(ia);
+    ib = __builtin_amdgcn_readfirstlane(ib);
+  }
+  auto skip = [&](int i) {
+    const int ph = i & 3;
+    issue_k(tile_at(i + 3), (ph + 3) & 3, i + 3 < n && partial_at(i + 3));
+    issue_v(tile_at(i + 3), (ph + 3) & 3);
+    vm_wait<2 * NDMA + NB>();
+    lds_barrier();
+  };
   f32x16_t sa, da, sb, db_;
-  if (n > 0) products(0, 0, sa, da);
+  for (int i = 0; i < ia; ++i) skip(i);
+  if (ia < ib) products(ia & 3, ia & 3, sa, da);
   // one step: tile i's S and dP are in (cs, cd); the next tile's products go to (ns, nd)
   auto step = [&](int i, f32x16_t& cs, f32x16_t& cd, f32x16_t& ns, f32x16_t& nd) {
     const int ph = i & 3;
@@ -1187,7 +1212,7 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
     vm_wait<2 * NDMA + NB>();
     lds_barrier();
   };
-  for (int i = 0; i < n; ++i) {
+  for (int i = ia; i < ib; ++i) {
     if constexpr (D <= 64) {
       step(i, sa, da, sa, da);
     } else {
@@ -1196,6 +1221,7 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
       da = db_;
     }
   }
+  for (int i = ib; i < n; ++i) skip(i);
   vm_wait<0>();  // no load may land in LDS after the workgroup ends
 
   if (qi < g.sq) {
