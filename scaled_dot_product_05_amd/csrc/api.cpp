@@ -872,7 +872,7 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     sq.max_items = int32_t(thd_items(a.s.total_q, a.s.batch, sq.tile_own));
     SchedParams sk = sched_params(a.s, false, reinterpret_cast<WorkItem*>(ws + w.wk_off),
                                   reinterpret_cast<int32_t*>(ws + w.ck_off));
-    sk.tile_own = bwd_k_rows(a.dtype);
+    sk.tile_own = bwd_k_tile_rows(p, DType(a.dtype));  // never more items than the workspace holds
     sk.tile_other = f32 ? 32 : kBwdKInner;
     sk.max_items = int32_t(thd_items(a.s.total_k, a.s.batch, sk.tile_own));
     if ((e = launch_schedule2(sq, sk, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");

@@ -17,7 +17,10 @@
 //         in registers.
 // With 16-byte aligned rows and head_dim 64 or 128, dq and dkdv are the pipelined kernels
 // near the end of this file (streamed tiles loaded straight into LDS, transposed operands
-// read with ds_read_b64_tr_b16) and run as one launch.  Otherwise the register-staged
+// read with ds_read_b64_tr_b16) and run as one launch; at head_dim 128 (no block mask, no
+// split) they run as two launches of four-wave workgroups instead, dq first (128 query
+// rows per workgroup, forming Delta and LSE log2(e) in place of the pre-pass), then dkdv
+// (128 keys per workgroup, the four waves sharing each Q/dO tile).  Otherwise the register-staged
 // kernels below keep the row-contracted operands (K in dq; Q and dO in dkdv) transposed in
 // LDS, written once per tile from the registers that fill the row-major copy, and split the
 // streamed tile between wave pairs so small problems still launch enough waves.  fp32 mode
@@ -1236,7 +1239,8 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
   }
 }
 
-// dK, dV.  A workgroup of 2 waves owns 64 keys of one kv head (lane = key) and streams
+// dK, dV.  A workgroup of W waves (2, or 4 in the separate head_dim-128 launch) owns 32 W
+// keys of one kv head, 32 per wave (lane = key), and streams
 // 32-row query tiles of every q head of its group:
 //   S  = Q K^T   (A: Q rows from LDS, B: K^T in registers)
 //   dP = dO V^T  (A: dO rows from LDS, B: V^T in registers)
@@ -1259,7 +1263,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   constexpr int NC = D / 16, NDB = D / 32, NPC = BQ / 16;
   constexpr int NS = DkdvP<D, W>::NS, SB = DkdvP<D, W>::SB;
   constexpr int NL = 2 * NDMA + 1 + (BSM ? 1 : 0);  // loads per wave per tile
-  static_assert(W == 2 && NDMA >= 1 && NPC == 2, "tile split");
+  static_assert((W == 2 || (W == 4 && !BSM && !SPLIT)) && NDMA >= 1 && NPC == 2, "tile split");
 
   const Shape& s = p.s;
   BwdPos w;
@@ -1406,7 +1410,8 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     for (int u = 0; u < NDMA; ++u) dma16(rq, dst + (u * W + wave) * 1024, qoff[u] + oq);
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) dma16(rg, dst + TB + (u * W + wave) * 1024, goff[u] + og);
-    if (lane < 32) dma4(rstat, dst + 2 * TB + wave * 128, uint32_t(delta_index(s, w.b, h, g, qbase + lane)) * 4u);
+    if (wave < 2 && lane < 32)
+      dma4(rstat, dst + 2 * TB + wave * 128, uint32_t(delta_index(s, w.b, h, g, qbase + lane)) * 4u);
     if constexpr (BSM) {
       // not partial: a load from past the buffer end (fills zeros, reads nothing)
       const i32x4_t rb = make_rsrc(s.bm.bits + bm_plane(s.bm, w.b, h) * s.sq * int64_t(s.bm.words),
@@ -1588,12 +1593,24 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   // head_dim <= 64 one pair of score registers: the current item's S and dP are taken into
   // their first uses before the next item's products are issued into the same registers
   // (no copies); head_dim 128 keeps two pairs and lets the compiler interleave (as in dQ).
+  // every load of this wave but the last tile's (waves 2 and 3 of a four-wave block load no
+  // LSE log2e or Delta)
+  auto wait_tiles = [&]() {
+    if constexpr (W == 2) {
+      vm_wait<NL>();
+    } else {
+      if (wave < 2)
+        vm_wait<NL>();
+      else
+        vm_wait<NL - 1>();
+    }
+  };
   f32x16_t sa, da, sb, db_;
   if (n > 0) {
     issue(0, 0);
     issue(1, 1);
     issue(2, 2);
-    vm_wait<NL>();
+    wait_tiles();
     lds_barrier();
     products(0, sa, da);
   }
@@ -1628,7 +1645,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
       update_at(ph, qt_c, false, x, y);
       advance(gi_c, qt_c);
     }
-    vm_wait<NL>();
+    wait_tiles();
     lds_barrier();
   };
   for (int it = 0; it < n; ++it) {
@@ -1995,6 +2012,11 @@ int bwd_q_tile_rows(const BwdParams& p, DType dt) {
   return dq_wide(p, dt) ? kBwdQ16Wide : kBwdQ16;
 }
 
+int bwd_k_tile_rows(const BwdParams& p, DType dt) {
+  if (dt == DType::F32) return kBwdK32;
+  return dq_wide(p, dt) ? kBwdK16Wide : kBwdK16;
+}
+
 template <int ES, bool BF>
 static hipError_t pre(const BwdParams& p, hipStream_t st) {
   const Shape& s = p.s;
@@ -2020,7 +2042,7 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
         // dQ first: its blocks form Delta and LSE log2(e) of their rows for dK/dV (no pre-pass)
         hipError_t e = go(bwd_dq16p_kernel<BF, D, 4, true>, "bwd_dq", bq, st, p, 256);
         if (e != hipSuccess) return e;
-        return go(bwd_dkdv16p_kernel<BF, D, 2>, "bwd_dkdv", bk, st, p, 128);
+        return go(bwd_dkdv16p_kernel<BF, D, 4>, "bwd_dkdv", bk, st, p, 256);
       }
     }
     if (kv && q) {
@@ -2108,7 +2130,7 @@ hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
                                      : (dt == DType::BF16 ? pre<2, true>(p, st) : pre<2, false>(p, st));
     if (e != hipSuccess) return e;
   }
-  const int tq = bwd_q_tile_rows(p, dt), tk = dt == DType::F32 ? kBwdK32 : kBwdK16;
+  const int tq = bwd_q_tile_rows(p, dt), tk = bwd_k_tile_rows(p, dt);
   int64_t bq = s.thd ? ((s.total_q + tq - 1) / tq + s.batch) * s.hq : int64_t((s.sq + tq - 1) / tq) * s.batch * s.hq;
   int64_t bk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk : int64_t((s.sk + tk - 1) / tk) * s.batch * s.hk;
   switch (dt) {

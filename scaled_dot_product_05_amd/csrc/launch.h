@@ -21,6 +21,8 @@ hipError_t launch_bwd(const BwdParams& p, DType dtype, hipStream_t stream);
 // Query rows per dQ tile (and THD dQ work item) of the kernels launch_bwd picks for p
 // (strides, alignment, head_dim, block mask and split set).
 int bwd_q_tile_rows(const BwdParams& p, DType dtype);
+// Keys per dK/dV tile (and THD dK/dV work item), likewise.
+int bwd_k_tile_rows(const BwdParams& p, DType dtype);
 hipError_t launch_merge_fwd(const MergeParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_merge_bwd(const MergeParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_block_mask_build(const BmBuildParams& p, hipStream_t stream);

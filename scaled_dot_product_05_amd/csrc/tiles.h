@@ -38,6 +38,8 @@ constexpr int kBwdQInner = 64;
 // rows of every head of the group stream in kBwdKInner tiles (16-bit) or 32-row tiles (fp32)
 constexpr int kBwdK16 = 64;
 constexpr int kBwdK32 = 128;
+// keys per workgroup of the separate four-wave head_dim-128 dK/dV launch
+constexpr int kBwdK16Wide = 128;
 constexpr int kBwdKInner = 64;
 
 // backward: queries and keys per sequence up to which every wave is a work unit of its own

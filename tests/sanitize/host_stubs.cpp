@@ -22,6 +22,7 @@ hipError_t launch_fwd8(const FwdParams&, hipStream_t) { return hipErrorNotSuppor
 bool fwd8_ok(const FwdParams&) { return false; }
 hipError_t launch_bwd(const BwdParams&, DType, hipStream_t) { return hipErrorNotSupported; }
 int bwd_q_tile_rows(const BwdParams&, DType) { return 64; }
+int bwd_k_tile_rows(const BwdParams&, DType) { return 64; }
 hipError_t launch_merge_fwd(const MergeParams&, DType, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_merge_bwd(const MergeParams&, DType, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_block_mask_build(const BmBuildParams&, hipStream_t) { return hipErrorNotSupported; }
