@@ -391,19 +391,6 @@ struct BwdWs {
 int bwd_q_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdQ32 : kBwdQ16; }
 int bwd_k_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdK32 : kBwdK16; }
 
-// Compute units of the current device (0 if unknown), cached per device.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      return 0;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 // Split dK/dV blocks: GQA groups, 16-bit inputs, head_dim 64 or 128, no block mask, and a
 // small grid (at most kBwdSplitPerCU dK/dV plus dQ blocks per CU of the current device),
@@ -711,6 +698,20 @@ SchedParams sched_params(const Shape& s, bool q_items, WorkItem* items, int32_t*
 }  // namespace
 
 namespace sdpa {
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Record an error message for sdpa_last_error() from another translation unit.
 int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
 int clear_error() { return ok(); }

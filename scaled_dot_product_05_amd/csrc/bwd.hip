@@ -971,7 +971,7 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
       // its butterfly over the row's 16 chunks.  This lane holds chunks c = 2 cc + hf, so the
       // partners c^8, c^4, c^2 are chunks cc^4, cc^2, cc^1 of this lane and c^1 is the same
       // chunk of lane l^32.
-      static_assert(NC == 8, "the butterfly below is the pre-pass's at head_dim 128");
+      static_assert(NC == 8 || NC == 4, "the butterfly below is the pre-pass's at head_dim 128 and 64");
       const uint16_t* ob = static_cast<const uint16_t*>(p.o.ptr) + w.b * p.o.sb + w.h * p.o.sh + g.qrow0 * p.o.ss;
       float pc[NC];
 #pragma unroll
@@ -983,7 +983,11 @@ __device__ __forceinline__ void dq16p_body(const BwdParams& p, lds_t* const lds,
           d = __builtin_fmaf(to_f32<BF>(uint16_t(elem16(ov, e))), to_f32<BF>(uint16_t(elem16(gf[cc], e))), d);
         pc[cc] = d;
       }
-      float dot = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
+      float dot;
+      if constexpr (NC == 8)
+        dot = ((pc[0] + pc[4]) + (pc[2] + pc[6])) + ((pc[1] + pc[5]) + (pc[3] + pc[7]));
+      else  // head_dim 64: 8 chunks a row, partners c^4, c^2 in this lane (cc^2, cc^1)
+        dot = (pc[0] + pc[2]) + (pc[1] + pc[3]);
       dot += __shfl_xor(dot, 32);
       if (qi < g.sq) {
         const float l = p.lse.ptr[w.b * p.lse.sb + w.h * p.lse.sh + (g.qrow0 + qi) * p.lse.ss];
@@ -1993,18 +1997,33 @@ static bool pipelined_ok(const BwdParams& p, int64_t rows, int64_t ss_a, int64_t
          (rows + 4 * 64) * ss * 2 < (int64_t(1) << 31);
 }
 
-// head_dim 128, 16-bit, both pipelined kernels usable, no block mask and no dK/dV split:
-// dK/dV and dQ run as two launches, dQ with four waves per 128-row tile (two waves per SIMD;
-// in the fused launch both halves run at the dK/dV kernel's one wave per SIMD).  Measured:
+// head_dim 64 or 128, 16-bit, both pipelined kernels usable, no block mask, no dK/dV split
+// and a large grid: dQ and dK/dV run as two launches of four-wave workgroups (at D128 the dQ
+// half then runs two waves per SIMD instead of the dK/dV body's one; both halves share each
+// streamed tile between four waves, and dQ forms Delta in place of the pre-pass).  Measured:
 // B8 S4096 H16/4 backward 2180 -> 2010 us, H16/16 2175 -> 2040 us; varlen THD GQA (C4) 802
 // -> 811 us of kernels but a 0.5% shorter step (the fused launch filled the tail of the
 // longest dK/dV chain with dQ blocks).  Splitting the long dK/dV blocks into halves in the
 // separate launch took 495 -> 871 us (each half's release of its partial sums).
+template <int D>
+static bool dq_wide_d(const BwdParams& p) {
+  return pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV) &&
+         pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ) &&
+         (p.aligned & kAlO) && p.o.ss >= D;
+}
+// The two launches pay off once the fused launch would have more than kBwdWideMinPerCU
+// dK/dV plus dQ blocks per CU of the current device; on smaller grids the fused launch
+// fills the tail of each half with the other (measured, causal bf16: D64 B1 S4096 H8
+// fused 107 vs 163 us, B4 S2048 85 vs 101 us, B4 S4096 280 vs 275 us, B8 S4096 530 vs
+// 500 us; D128 H16 B4 S1024 106 vs 113 us, B2 S2048 163 vs 164 us, B2 S4096 546 vs 515 us).
 static bool dq_wide(const BwdParams& p, DType dt) {
-  return dt != DType::F32 && p.s.d == 128 && !p.s.bm.bits && p.nsplit != 2 &&
-         pipelined_ok<128>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV) &&
-         pipelined_ok<128>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ) &&
-         (p.aligned & kAlO) && p.o.ss >= 128;
+  const Shape& s = p.s;
+  if (dt == DType::F32 || s.bm.bits || p.nsplit == 2) return false;
+  if (!(s.d == 128 ? dq_wide_d<128>(p) : (s.d == 64 && dq_wide_d<64>(p)))) return false;
+  const int64_t tq = kBwdQ16, tk = kBwdK16;
+  const int64_t nq = s.thd ? ((s.total_q + tq - 1) / tq + s.batch) * s.hq : ((s.sq + tq - 1) / tq) * s.batch * s.hq;
+  const int64_t nk = s.thd ? ((s.total_k + tk - 1) / tk + s.batch) * s.hk : ((s.sk + tk - 1) / tk) * s.batch * s.hk;
+  return nq + nk > int64_t(kBwdWideMinPerCU) * device_cus();
 }
 
 int bwd_q_tile_rows(const BwdParams& p, DType dt) {
@@ -2037,7 +2056,7 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
     static_assert(kBwdQ16 == 64 && kBwdK16 == 64, "tile rows of the pipelined kernels");
     const bool kv = pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV);
     const bool q = pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
-    if constexpr (D == 128) {
+    if constexpr (D == 128 || D == 64) {
       if (dq_wide(p, BF ? DType::BF16 : DType::F16)) {
         // dQ first: its blocks form Delta and LSE log2(e) of their rows for dK/dV (no pre-pass)
         hipError_t e = go(bwd_dq16p_kernel<BF, D, 4, true>, "bwd_dq", bq, st, p, 256);

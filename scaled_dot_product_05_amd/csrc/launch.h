@@ -23,6 +23,8 @@ hipError_t launch_bwd(const BwdParams& p, DType dtype, hipStream_t stream);
 int bwd_q_tile_rows(const BwdParams& p, DType dtype);
 // Keys per dK/dV tile (and THD dK/dV work item), likewise.
 int bwd_k_tile_rows(const BwdParams& p, DType dtype);
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus();
 hipError_t launch_merge_fwd(const MergeParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_merge_bwd(const MergeParams& p, DType dtype, hipStream_t stream);
 hipError_t launch_block_mask_build(const BmBuildParams& p, hipStream_t stream);

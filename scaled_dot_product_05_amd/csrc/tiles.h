@@ -31,15 +31,18 @@ constexpr int kFwdShortMinB = 3;  // its workgroups per CU, head_dim <= 64
 // in kBwdQInner tiles (16-bit) or 32-key tiles (fp32)
 constexpr int kBwdQ16 = 64;
 constexpr int kBwdQ32 = 128;
-// dQ rows per tile of the separate four-wave head_dim-128 dQ launch
+// dQ rows per tile of the separate four-wave dQ launch
 constexpr int kBwdQ16Wide = 128;
 constexpr int kBwdQInner = 64;
 // backward dK/dV: one workgroup owns kBwdK16 / kBwdK32 keys of one (batch, kv head); query
 // rows of every head of the group stream in kBwdKInner tiles (16-bit) or 32-row tiles (fp32)
 constexpr int kBwdK16 = 64;
 constexpr int kBwdK32 = 128;
-// keys per workgroup of the separate four-wave head_dim-128 dK/dV launch
+// keys per workgroup of the separate four-wave dK/dV launch
 constexpr int kBwdK16Wide = 128;
+// fused-launch blocks (dK/dV plus dQ, 64-row tiles) per CU above which the backward runs as
+// the two four-wave launches
+constexpr int kBwdWideMinPerCU = 12;
 constexpr int kBwdKInner = 64;
 
 // backward: queries and keys per sequence up to which every wave is a work unit of its own

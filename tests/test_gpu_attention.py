@@ -201,18 +201,18 @@ def test_gqa_backward_split_thd():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("window,align", [((-1, 0), 0), ((70, 5), 1), ((-1, -1), 0)])
-def test_head_dim_128_dq_first_backward_with_dlse(dtype, window, align):
-    # One kv head per q head, so no dK/dV split: at head_dim 128 the backward runs the
-    # four-wave dQ launch (which also forms Delta and LSE log2e of its rows) and then dK/dV.
-    # Ragged lengths (neither a multiple of the 128-row dQ tile nor of the 32-row dK/dV
-    # item), a given dLSE, and windows that leave some rows without a visible key.
+def test_head_dim_128_backward_with_dlse(dtype, window, align):
+    # Head_dim 128 with one kv head per q head (no dK/dV split) on a small grid (the fused
+    # launch after the pre-pass): ragged lengths (neither a multiple of the 64-row tiles nor
+    # of the 32-row dK/dV item), a given dLSE, and windows that leave some rows without a
+    # visible key.  Large grids of the same kind are in test_gpu_target.
     w = synth.dense(31, 990, dtype, "bshd", 2, 333, 290, 3, 3, 128, 0.09, window, align,
-                    with_grad=True, with_dlse=True, name="d128_dq_first")
+                    with_grad=True, with_dlse=True, name="d128_dlse")
     run_case(w, dlse=True)
 
 
-def test_head_dim_128_dq_first_backward_thd():
-    # the same path over THD, with empty and one-row sequences
+def test_head_dim_128_backward_thd_dlse():
+    # the same over THD, with empty and one-row sequences
     w = synth.thd(32, 991, "bf16", [1, 0, 130, 257, 0, 300, 64, 129], 4, 4, 128, 0.088,
                   (-1, 0), with_grad=True, with_dlse=True)
     run_case(w, dlse=True)

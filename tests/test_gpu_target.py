@@ -79,3 +79,51 @@ def test_target_backward_sampled(b, s, h, hk, d):
     say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= G_TOL["bf16"], f"{n}: {e}"
+
+
+# Grids above 12 fused-launch blocks per CU (of 256) take the two four-wave launches (dQ,
+# which also forms Delta from dLSE, then dK/dV); ragged S, windows and a given dLSE.
+TWO_LAUNCH = [(5, 3000, 8, 8, 64, (512, 0)), (4, 3000, 16, 4, 128, (-1, 0)),
+              (3, 3000, 16, 16, 128, (300, 20))]
+
+
+@pytest.mark.parametrize("b,s,h,hk,d,window", TWO_LAUNCH)
+def test_two_launch_backward_sampled(b, s, h, hk, d, window):
+    import scaled_dot_product_05_amd as S
+    w = synth.dense(5, 960, "bf16", "bshd", b, s, s, h, hk, d, d ** -0.5, window, 0,
+                    with_grad=True, with_dlse=True, name="two_launch")
+    say(f"case two-launch backward B{b} S{s} H{h}/{hk} D{d} window {window}")
+    q, k, v, g, dl = (t.to(DEV) for t in (w.q, w.k, w.v, w.dout, w.dlse))
+    o, lse = gpu_forward(w, q, k, v)
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(True)
+    dq, dk, dv = gpu_backward(w, q, k, v, o, lse, g, dlse=dl)
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(False)
+    launched = set(S.sdpa_profile_read())
+    assert {"bwd_dq", "bwd_dkdv"} <= launched and "bwd_pre" not in launched, launched
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    rng = np.random.default_rng(13)
+    group = h // hk
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for bb, kh in [(0, 0), (b - 1, hk - 1)]:
+        heads = list(range(kh * group, (kh + 1) * group))
+        kg, vg = synth.f64(w.k[bb, :, kh]), synth.f64(w.v[bb, :, kh])
+        qh = np.stack([synth.f64(w.q[bb, :, hh]) for hh in heads])
+        gh = np.stack([synth.f64(w.dout[bb, :, hh]) for hh in heads])
+        dlh = np.stack([synth.f64(w.dlse[bb, hh]) for hh in heads])
+        rows = _rows(s, rng)
+        for i, hh in enumerate(heads[:2]):
+            got["dq"].append(synth.f64(dq[bb, rows, hh]))
+            ref["dq"].append(oracle.dq_rows(qh[i], kg, vg, gh[i], w.scale, rows, window, 0, dlh[i]))
+        cols = _rows(s, rng)
+        rk, rv = oracle.dkdv_cols(qh, kg, vg, gh, w.scale, cols, window, 0, dlh)
+        got["dk"].append(synth.f64(dk[bb, cols, kh]))
+        got["dv"].append(synth.f64(dv[bb, cols, kh]))
+        ref["dk"].append(rk)
+        ref["dv"].append(rv)
+    errs = {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= G_TOL["bf16"], f"{n}: {e}"
