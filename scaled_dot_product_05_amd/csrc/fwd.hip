@@ -461,6 +461,16 @@ __global__ __launch_bounds__(kThreads, (D == 64 && MINB < 3) ? 3 : MINB) void fw
     wf1 = int(clamp64(b, wf0, int64_t(1) << 30));
   }
 
+  // This wave's step bound: after the last key tile one of its rows sees (the block's later
+  // tiles are masked for it below the causal diagonal, and all of them for a wave past the
+  // sequence end) it only issues its loads and meets the barriers.
+  int wb = 1 << 30;
+  if constexpr (!BSM) {
+    int wj0 = 0, wj1 = 0;
+    if (qw0 < qw1) key_range(s, g, qw0, qw1, wj0, wj1);
+    wb = __builtin_amdgcn_readfirstlane(wj1 > wj0 ? (wj1 + BN - 1) / BN - kt0 : 0);
+  }
+
   const float c = fmaxf(fabsf(s.scale_log2), 1e-30f);
   const uint32_t qsign = s.scale_log2 < 0.f ? 0x80008000u : 0u;
   uint4 qf[QB][NC];
@@ -728,11 +738,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && MINB < 3) ? 3 : MINB) void fw
     issue_k(tile_at(i + NS), ph);
     issue_v(tile_at(i + NS - 1), (ph + NS - 1) % NS);
     issue_bits(i + NS - 1, (ph + NS - 1) % NS);
-    mask(tile_at(i), partial_at(i), ph, cur);
-    uint4 pf[QB][NPC];
-    scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
-    softmax(cur, pf);
-    pv(std::integral_constant<int, ph>(), pf);
+    if (i < wb) {
+      mask(tile_at(i), partial_at(i), ph, cur);
+      uint4 pf[QB][NPC];
+      scores(std::integral_constant<int, (ph + 1) % NS>(), nxt);
+      softmax(cur, pf);
+      pv(std::integral_constant<int, ph>(), pf);
+    }
     vm_wait<(NS - 2) * (2 * NDMA + NB)>();
     lds_barrier();
   };
