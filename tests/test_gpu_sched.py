@@ -1,0 +1,78 @@
+"""THD work lists past the scheduler's one-pass sizes: more sequences than its workgroup has
+waves (16) and more items in one list than it has threads (1024), through the C ABI against
+the fp64 oracle (TE 885's packed THD layout with int32 cu_seqlens)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (DEV, G_TOL, LSE_TOL, O_TOL, check_forward, check_grads, cu_dev, gpu_backward,
+                      gpu_bhsd, gpu_forward, oracle_backward, oracle_forward, rel_err, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_thd_more_than_64_sequences():
+    rng = np.random.default_rng(70)
+    lengths = rng.integers(0, 90, 70).tolist()
+    lengths[5] = 0
+    lengths[40] = 200
+    w = synth.thd(31, 1100, "bf16", lengths, 4, 2, 64, 0.125, (-1, 0), with_grad=True,
+                  with_dlse=True)
+    say(f"case thd 70 sequences total {sum(lengths)}")
+    q, k, v = to_dev(w)
+    cq, ck = cu_dev(w)
+    o, lse = gpu_forward(w, q, k, v, cq, ck)
+    torch.cuda.synchronize()
+    check_forward(gpu_bhsd(o, w), synth.f64(lse), *oracle_forward(w), "bf16", "fwd")
+    dl = w.dlse.to(DEV)
+    dq, dk, dv = gpu_backward(w, q, k, v, o, lse, w.dout.to(DEV), dl, cq, ck)
+    torch.cuda.synchronize()
+    refs = oracle_backward(w, synth.f64(w.dlse))
+    check_grads([gpu_bhsd(t, w) for t in (dq, dk, dv)], refs, "bf16", "bwd")
+
+
+def test_thd_more_than_1024_tiles_sampled():
+    # 64 sequences of 2050-2200 rows: at least 17 query tiles of 128 rows each (and twice as
+    # many of 64), over 1024 items in one list; GQA 2/1
+    rng = np.random.default_rng(71)
+    lengths = rng.integers(2050, 2201, 64).tolist()
+    w = synth.thd(32, 1200, "bf16", lengths, 2, 1, 64, 0.125, (-1, 0), with_grad=True)
+    say("case thd 64 x 2050-2200 rows")
+    q, k, v = to_dev(w)
+    cq, ck = cu_dev(w)
+    o, lse = gpu_forward(w, q, k, v, cq, ck)
+    dq, dk, dv = gpu_backward(w, q, k, v, o, lse, w.dout.to(DEV), None, cq, ck)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
+    cu = w.cu_seqlens_q
+    worst_o = worst_l = 0.0
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        n = b - a
+        rows = np.unique(np.concatenate([[0, 127, 128, n - 1], rng.integers(0, n, 2)]))
+        hh = s % 2
+        qs, gs = (synth.f64(t[a:b, hh]) for t in (w.q, w.dout))
+        ks, vs = (synth.f64(t[a:b, 0]) for t in (w.k, w.v))
+        ro, rl = oracle.forward_rows(qs, ks, vs, w.scale, rows, w.window)
+        worst_o = max(worst_o, float(np.abs(synth.f64(o[a + rows, hh]) - ro).max()))
+        worst_l = max(worst_l, float(np.abs(synth.f64(lse[hh, a + rows]) - rl).max()))
+        got["dq"].append(synth.f64(dq[a + rows, hh]))
+        ref["dq"].append(oracle.dq_rows(qs, ks, vs, gs, w.scale, rows, w.window))
+        if s % 21 == 0:  # dK, dV sum over every query row of both q heads: four sequences
+            qh = np.stack([synth.f64(w.q[a:b, i]) for i in range(2)])
+            gh = np.stack([synth.f64(w.dout[a:b, i]) for i in range(2)])
+            rk, rv = oracle.dkdv_cols(qh, ks, vs, gh, w.scale, rows, w.window)
+            got["dk"].append(synth.f64(dk[a + rows, 0]))
+            got["dv"].append(synth.f64(dv[a + rows, 0]))
+            ref["dk"].append(rk)
+            ref["dv"].append(rv)
+    errs = {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    say(f"  sampled: max |O err| {worst_o:.2e}, max |LSE err| {worst_l:.2e}, " +
+        ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
+    assert worst_o <= O_TOL["bf16"] and worst_l <= LSE_TOL
+    for n, e in errs.items():
+        assert e <= G_TOL["bf16"], f"{n}: {e}"
