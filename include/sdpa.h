@@ -244,8 +244,10 @@ int sdpa_fwd_fp8(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_ten
  * LSE_i * log2(e) for every q row, plus the THD work lists, plus under GQA on small grids
  * (16-bit inputs, head_dim 64 or 128, no block mask, at most 8 work blocks per compute unit
  * of the current device) the fp32 partial dK/dV sums of the two halves of every 64-key block
- * (1 KiB x head_dim per block) and one counter per block.  Host only; query it with the
- * device that will run the call current. */
+ * (1 KiB x head_dim per block) and one counter per block, plus for THD on large grids (16-bit,
+ * head_dim 64 or 128, no block mask, more than 12 work blocks per compute unit) up to 32 MiB
+ * of fp32 partial dK/dV sums for the longest key tiles, which may run as two halves.  Host
+ * only; query it with the device that will run the call current. */
 int sdpa_bwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes);
 
 /* Host-only dry run of sdpa_bwd's validation. */

@@ -386,6 +386,7 @@ size_t fwd_ws_bytes(const Shape& s, int32_t dtype) {
 struct BwdWs {
   int64_t delta_off, lse2_off, wq_off, cq_off, wk_off, ck_off, total;
   int64_t split_blocks, cnt_off, part_off;  // split dK/dV (split_blocks = 0: none)
+  int64_t ksplit_cap, kcnt_off, kpart_off;  // split THD dK/dV items (ksplit_cap = 0: none)
 };
 
 int bwd_q_rows(int32_t dtype) { return dtype == SDPA_DTYPE_F32 ? kBwdQ32 : kBwdQ16; }
@@ -408,19 +409,36 @@ bool bwd_split_ok(const Shape& s, int32_t dtype) {
   return nk + nq <= int64_t(kBwdSplitPerCU) * device_cus() && nk * 2 < (int64_t(1) << 30);
 }
 
+// THD, 16-bit, head_dim 64 or 128, no block mask, on a grid large enough for the separate
+// dK/dV launch (more than kBwdWideMinPerCU fused blocks per CU): room for the partial sums of
+// split items, 2 halves x 128 keys x D x {dK, dV} in fp32 per item and kv head, up to 32 MiB
+// (at most 64 items).  The launcher decides on the strides whether the launch is used.
+int64_t bwd_ksplit_cap(const Shape& s, int32_t dtype) {
+  if (!s.thd || dtype == SDPA_DTYPE_F32 || dtype == SDPA_DTYPE_FP8_E4M3 || (s.d != 64 && s.d != 128) ||
+      s.bm.bits || s.hk < 1)
+    return 0;
+  const int64_t tk = kBwdK16, tq = kBwdQ16;
+  const int64_t nk = ((s.total_k + tk - 1) / tk + s.batch) * s.hk;
+  const int64_t nq = ((s.total_q + tq - 1) / tq + s.batch) * s.hq;
+  if (nq + nk <= int64_t(kBwdWideMinPerCU) * device_cus()) return 0;
+  const int64_t per = int64_t(s.hk) * 2 * kBwdK16Wide * s.d * 2 * 4;
+  return std::max<int64_t>(1, std::min<int64_t>(64, (int64_t(32) << 20) / per));
+}
+
 BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
   BwdWs w{};
   int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
   w.delta_off = 0;
   w.lse2_off = round_up(rows * 4, 256);
   int64_t off = round_up(w.lse2_off + rows * 4, 256);
+  w.ksplit_cap = bwd_ksplit_cap(s, dtype);
   if (s.thd) {
     w.wq_off = off;
     off = round_up(off + thd_items(s.total_q, s.batch, bwd_q_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
     w.cq_off = off;
     off += 256;
-    w.wk_off = off;
-    off = round_up(off + thd_items(s.total_k, s.batch, bwd_k_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
+    w.wk_off = off;  // (a split item takes two entries)
+    off = round_up(off + (thd_items(s.total_k, s.batch, bwd_k_rows(dtype)) + w.ksplit_cap) * int64_t(sizeof(WorkItem)), 256);
     w.ck_off = off;
     off += 256;
   }
@@ -434,6 +452,12 @@ BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
     off = round_up(off + w.split_blocks * 4, 256);
     w.part_off = off;
     off = round_up(off + w.split_blocks * 2 * 64 * int64_t(s.d) * 2 * 4, 256);
+  }
+  if (w.ksplit_cap > 0) {
+    w.kcnt_off = off;
+    off += 256;
+    w.kpart_off = off;
+    off = round_up(off + w.ksplit_cap * s.hk * 2 * kBwdK16Wide * int64_t(s.d) * 2 * 4, 256);
   }
   w.total = off;
   return w;
@@ -862,6 +886,12 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     p.split_cnt = reinterpret_cast<int32_t*>(ws + w.cnt_off);
     p.split_part = reinterpret_cast<float*>(ws + w.part_off);
   }
+  if (w.ksplit_cap > 0) {
+    p.ksplit_cap = int32_t(w.ksplit_cap);
+    p.ksplit_count = reinterpret_cast<int32_t*>(ws + w.kcnt_off);
+    p.ksplit_part = reinterpret_cast<float*>(ws + w.kpart_off);
+    p.ksplit_cap = bwd_k_split_cap(p, DType(a.dtype));
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (a.s.thd) {
@@ -876,6 +906,15 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
     sk.tile_own = bwd_k_tile_rows(p, DType(a.dtype));  // never more items than the workspace holds
     sk.tile_other = f32 ? 32 : kBwdKInner;
     sk.max_items = int32_t(thd_items(a.s.total_k, a.s.batch, sk.tile_own));
+    if (p.ksplit_cap > 0) {
+      // split the items whose chain of (q head, q tile) steps exceeds the mean per dK/dV
+      // workgroup slot (one per CU at head_dim 128, two at 64); a split item takes two entries
+      sk.max_items += p.ksplit_cap;
+      sk.split_cap = p.ksplit_cap;
+      sk.split_heads = a.s.hk;
+      sk.split_slots = device_cus() * (a.s.d == 128 ? 1 : 2);
+      sk.nsplit = const_cast<int32_t*>(p.ksplit_count);
+    }
     if ((e = launch_schedule2(sq, sk, st)) != hipSuccess) return hip_fail(e, "THD schedule launch");
     p.work_q = sq.items;
     p.count_q = sq.count;

@@ -17,10 +17,12 @@
 //         in registers.
 // With 16-byte aligned rows and head_dim 64 or 128, dq and dkdv are the pipelined kernels
 // near the end of this file (streamed tiles loaded straight into LDS, transposed operands
-// read with ds_read_b64_tr_b16) and run as one launch; at head_dim 128 (no block mask, no
+// read with ds_read_b64_tr_b16) and run as one launch; on large grids (no block mask, no
 // split) they run as two launches of four-wave workgroups instead, dq first (128 query
 // rows per workgroup, forming Delta and LSE log2(e) in place of the pre-pass), then dkdv
-// (128 keys per workgroup, the four waves sharing each Q/dO tile).  Otherwise the register-staged
+// (128 keys per workgroup, the four waves sharing each Q/dO tile); under THD the longest
+// dkdv items may run as two half blocks whose fp32 partial sums a combine launch adds (no
+// atomics: each half writes its own slot).  Otherwise the register-staged
 // kernels below keep the row-contracted operands (K in dq; Q and dO in dkdv) transposed in
 // LDS, written once per tile from the registers that fill the row-major copy, and split the
 // streamed tile between wave pairs so small problems still launch enough waves.  fp32 mode
@@ -97,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 // ----------------------------------------------------------------------------------------
 struct BwdPos {
   int b, h, tile;
+  int item = 0;   // THD: index in the work list
 };
 
 // GROUPED (head_dim 128 kernels): THD grids with a multiple of 8 heads give each XCD a
@@ -123,6 +126,7 @@ __device__ __forceinline__ bool bwd_decode(const Shape& s, const WorkItem* work,
       h = bid % heads;
     }
     w.h = h;
+    w.item = item;
     if (item >= *count) return false;
     WorkItem it = work[item];
     w.b = it.seq;
@@ -1260,7 +1264,8 @@ struct DkdvP {
   static constexpr int LDS = NS * SB;
 };
 
-template <bool BF, int D, int W, bool BSM, bool SPLIT = false>
+// HALVES (separate THD launch): split items of the list come as two half blocks (see below)
+template <bool BF, int D, int W, bool BSM, bool SPLIT = false, bool HALVES = false>
 __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const lds, int bid, int split = 0) {
   constexpr int BK = 32 * W, BQ = DkdvP<D, W>::BQ, NT = 64 * W;
   constexpr int CPR = D / 8, TB = DkdvP<D, W>::TB, NDMA = BQ * CPR / NT;
@@ -1271,7 +1276,16 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
 
   const Shape& s = p.s;
   BwdPos w;
+  static_assert(!HALVES || (W == 4 && !BSM && !SPLIT), "halves: the separate launch only");
   if (!bwd_decode<(D >= 128)>(s, p.work_k, p.count_k, s.hk, s.sk, BK, false, w, bid)) return;
+  // a split THD item comes twice in the list, with (half + 1) << 24 in its tile field; its
+  // halves' partial-sum slot is the pair's index
+  int half = -1, slot = 0;
+  if constexpr (HALVES) {
+    half = (w.tile >> 24) - 1;
+    w.tile &= 0xffffff;
+    slot = w.item >> 1;
+  }
   const Seq g = seq_of(s, w.b);
   const int k0 = w.tile * BK;
   if (k0 >= g.sk) return;
@@ -1320,11 +1334,13 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     __syncthreads();
   }
   const int n_all = n;  // items of the whole block (before a split)
-  // a split block takes the first or the second half of the items
+  // a split block (or half of a split THD item) takes the first or the second half of the
+  // items
   int ib = 0;
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT) half = split;
+  if (SPLIT || (HALVES && half >= 0)) {
     const int n1 = (n + 1) / 2;
-    if (split == 0) {
+    if (half == 0) {
       n = n1;
     } else {
       ib = n1;
@@ -1333,7 +1349,7 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
   }
   // item it -> q head (within the group), q tile, and whether its block needs the bits
   auto item = [&](int it, int& gi, int& qt, bool& part) {
-    if constexpr (SPLIT) it += ib;
+    if constexpr (SPLIT || HALVES) it += ib;
     if constexpr (BSM) {
       // the same order as without a mask: last listed tile first; one shared list: every q
       // head at one tile before the next, per-head lists: head after head (last head first)
@@ -1692,6 +1708,20 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
         adv[db][r] += other[((NDB + db) * 16 + r) * 64 + lane];
       }
   }
+  if (HALVES && half >= 0) {
+    // half of a split THD item: fp32 partial sums in register order, one 256-byte row per
+    // register, for the combine launch
+    constexpr int PR = 2 * NDB * 16 * 64;  // floats per wave
+    float* mine = p.ksplit_part + ((int64_t(slot) * s.hk + hk) * 2 + half) * (PR * W) + wave * PR;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mine[(db * 16 + r) * 64 + lane] = adk[db][r];
+        mine[((NDB + db) * 16 + r) * 64 + lane] = adv[db][r];
+      }
+    return;
+  }
   if (kj < g.sk) {
     uint16_t* krow = dkb + kj * p.dk.ss;
     uint16_t* vrow = dvb + kj * p.dv.ss;
@@ -1717,10 +1747,45 @@ __global__ __launch_bounds__(64 * W, (D == 128 && W == 2) ? 1 : 2) void bwd_dq16
   dq16p_body<BF, D, W, false, DELTA>(p, (lds_t*)smem_, blockIdx.x);
 }
 
-template <bool BF, int D, int W>
+template <bool BF, int D, int W, bool HALVES = false>
 __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 2) void bwd_dkdv16p_kernel(BwdParams p) {
   __shared__ __align__(16) char smem_[DkdvP<D, W>::LDS];
-  dkdv16p_body<BF, D, W, false>(p, (lds_t*)smem_, blockIdx.x);
+  dkdv16p_body<BF, D, W, false, false, HALVES>(p, (lds_t*)smem_, blockIdx.x);
+}
+
+// The split THD items of the separate dK/dV launch: block (slot, kv head) adds the two halves'
+// partial sums in a fixed order (first + second) and writes dK (scaled) and dV as the dK/dV
+// body's own epilogue does, the same lane for the same (key, d).
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_combine_kernel(BwdParams p) {
+  constexpr int W = 4, NDB = D / 32, PR = 2 * NDB * 16 * 64;
+  const Shape& s = p.s;
+  const int slot = blockIdx.x / s.hk, hk = blockIdx.x % s.hk;
+  if (slot >= *p.ksplit_count) return;
+  const WorkItem it = p.work_k[2 * slot];  // half 0 of the pair (tile | 1 << 24)
+  const Seq g = seq_of(s, it.seq);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5, wave = tid >> 6;
+  const int kj = (it.tile & 0xffffff) * (32 * W) + wave * 32 + l32;
+  if (kj >= g.sk) return;
+  const float* a = p.ksplit_part + (int64_t(slot) * s.hk + hk) * 2 * (PR * W) + wave * PR;
+  const float* c = a + PR * W;
+  uint16_t* krow = static_cast<uint16_t*>(p.dk.ptr) + it.seq * p.dk.sb + hk * p.dk.sh + (g.krow0 + kj) * p.dk.ss;
+  uint16_t* vrow = static_cast<uint16_t*>(p.dv.ptr) + it.seq * p.dv.sb + hk * p.dv.sh + (g.krow0 + kj) * p.dv.ss;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = db * 32 + 8 * gq + 4 * hf;
+      float vk[4], vv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * gq + e;
+        vk[e] = a[(db * 16 + r) * 64 + lane] + c[(db * 16 + r) * 64 + lane];
+        vv[e] = a[((NDB + db) * 16 + r) * 64 + lane] + c[((NDB + db) * 16 + r) * 64 + lane];
+      }
+      out4_16<BF>(krow + d, vk, s.scale, true, p.accumulate);
+      out4_16<BF>(vrow + d, vv, 1.f, true, p.accumulate);
+    }
 }
 
 // dK/dV and dQ in one launch: blocks [0, nk) take key tiles, the rest query tiles.  The two
@@ -2036,6 +2101,23 @@ int bwd_k_tile_rows(const BwdParams& p, DType dt) {
   return dq_wide(p, dt) ? kBwdK16Wide : kBwdK16;
 }
 
+// Split THD dK/dV items (their partial-sum slots): only on the separate dK/dV launch, and only
+// when an item could exceed 1.5 times the mean cost per workgroup slot (the scheduler's own
+// rule, decided there on the actual lengths).  The cost of a key tile is the number of
+// 64-row query tiles it sees, at most ceil(max q length / 64); under a causal mask a
+// sequence of L tokens costs about L^2 / (2 x 64 x 128) over its key tiles, and the sum of
+// squares of the lengths is at least total^2 / batch, which bounds the mean from below.
+int bwd_k_split_cap(const BwdParams& p, DType dt) {
+  const Shape& s = p.s;
+  if (!(s.thd && p.ksplit_cap > 0 && p.ksplit_count && p.ksplit_part && dq_wide(p, dt))) return 0;
+  const double slots = double(device_cus()) * (s.d == 128 ? 1 : 2);
+  if (slots <= 0 || s.batch <= 0) return 0;
+  const double mean_lo = double(s.total_k) * double(s.total_k) / s.batch /
+                         (2.0 * kBwdKInner * kBwdK16Wide) * s.hk / slots;
+  const double max_item = double((int64_t(s.sq) + kBwdKInner - 1) / kBwdKInner);
+  return max_item * 10 > mean_lo * 15 ? p.ksplit_cap : 0;
+}
+
 template <int ES, bool BF>
 static hipError_t pre(const BwdParams& p, hipStream_t st) {
   const Shape& s = p.s;
@@ -2061,7 +2143,13 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
         // dQ first: its blocks form Delta and LSE log2(e) of their rows for dK/dV (no pre-pass)
         hipError_t e = go(bwd_dq16p_kernel<BF, D, 4, true>, "bwd_dq", bq, st, p, 256);
         if (e != hipSuccess) return e;
-        return go(bwd_dkdv16p_kernel<BF, D, 4>, "bwd_dkdv", bk, st, p, 256);
+        if (p.ksplit_cap <= 0) return go(bwd_dkdv16p_kernel<BF, D, 4>, "bwd_dkdv", bk, st, p, 256);
+        // THD that may have items far above the mean: the longest items run as two half
+        // blocks each (listed first, ksplit_cap items at most), then a combine
+        const int64_t xk = int64_t(p.ksplit_cap) * p.s.hk;
+        e = go(bwd_dkdv16p_kernel<BF, D, 4, true>, "bwd_dkdv", bk + xk, st, p, 256);
+        if (e != hipSuccess) return e;
+        return go(bwd_dkdv_combine_kernel<BF, D>, "bwd_dkdv_combine", xk, st, p, 256);
       }
     }
     if (kv && q) {

@@ -23,6 +23,9 @@ hipError_t launch_bwd(const BwdParams& p, DType dtype, hipStream_t stream);
 int bwd_q_tile_rows(const BwdParams& p, DType dtype);
 // Keys per dK/dV tile (and THD dK/dV work item), likewise.
 int bwd_k_tile_rows(const BwdParams& p, DType dtype);
+// THD items of the separate dK/dV launch that may run as two halves (0: none), given the
+// partial-sum slots the workspace holds in p.ksplit_cap.
+int bwd_k_split_cap(const BwdParams& p, DType dtype);
 // Compute units of the current device (0 if unknown), cached per device.
 int device_cus();
 hipError_t launch_merge_fwd(const MergeParams& p, DType dtype, hipStream_t stream);

@@ -99,6 +99,11 @@ struct BwdParams {
   int32_t split_blocks;  // dK/dV blocks (counters)
   int32_t* split_cnt;
   float* split_part;
+  // THD, separate dK/dV launch: the first *ksplit_count items of work_k (the longest) run as
+  // two half blocks each, whose fp32 partial sums a combine launch adds; ksplit_cap = 0: none
+  int32_t ksplit_cap;          // most items split (the partial-sum slots)
+  const int32_t* ksplit_count;
+  float* ksplit_part;          // [slot][kv head][half][{dK, dV} 128 keys x D, register order]
 };
 
 struct MergeParams {
@@ -135,6 +140,10 @@ struct SchedParams {
   int32_t max_items;
   WorkItem* items;
   int32_t* count;
+  // split count (split_cap > 0): the number of items, at most split_cap, whose cost exceeds
+  // the mean cost per work slot, total cost x split_heads / split_slots
+  int32_t split_cap, split_heads, split_slots;
+  int32_t* nsplit;
 };
 
 }  // namespace sdpa

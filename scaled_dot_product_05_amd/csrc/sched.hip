@@ -63,14 +63,48 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedPair pp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int nwaves = kSchedThreads / 64;
   constexpr int PER = kSchedBuckets / kSchedThreads;
+  __shared__ unsigned long long total_cost;
+  __shared__ int max_cost, split_at;
   for (int i = tid; i < kSchedBuckets; i += kSchedThreads) hist[i] = 0;
+  if (tid == 0) {
+    total_cost = 0;
+    max_cost = 0;
+    split_at = 0;
+  }
   __syncthreads();
+  unsigned long long my_sum = 0;
+  int my_max = 0;
   for (int b = wave; b < p.batch; b += nwaves) {
     SeqLens L = sched_lens(p, b);
     int nt = (L.own + p.tile_own - 1) / p.tile_own;
-    for (int t = lane; t < nt; t += 64) atomicAdd(&hist[item_cost(p, L, t)], 1);
+    for (int t = lane; t < nt; t += 64) {
+      const int c = item_cost(p, L, t);
+      atomicAdd(&hist[c], 1);
+      if (p.split_cap > 0) {
+        my_sum += unsigned(c);
+        my_max = max(my_max, c);
+      }
+    }
+  }
+  if (p.split_cap > 0) {  // total and largest cost: wave sums, one LDS atomic per wave
+    for (int o = 32; o > 0; o >>= 1) {
+      my_sum += __shfl_xor(my_sum, o);
+      my_max = max(my_max, __shfl_xor(my_max, o));
+    }
+    if (lane == 0) {
+      atomicAdd(&total_cost, my_sum);
+      atomicMax(&max_cost, my_max);
+    }
   }
   __syncthreads();
+  // Split items: those of cost above the mean per work slot, thr, when the largest cost
+  // exceeds 1.5 thr (below that the tail of the unsplit list costs less than the halves'
+  // partial sums and their combine); they are the list's first split_at entries.
+  int64_t thr = kSchedBuckets;
+  if (p.split_cap > 0 && p.split_slots > 0) {
+    thr = int64_t(total_cost) * p.split_heads / p.split_slots;
+    if (int64_t(max_cost) * 10 <= thr * 15) thr = kSchedBuckets;
+  }
   // exclusive scan in decreasing cost order: thread i owns reversed buckets PER*i .. PER*i+PER-1
   int local = 0;
   for (int k = 0; k < PER; ++k) local += hist[kSchedBuckets - 1 - (PER * tid + k)];
@@ -89,23 +123,32 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedPair pp) {
     int c = kSchedBuckets - 1 - (PER * tid + k);
     int n = hist[c];
     hist[c] = run;  // becomes the next free slot of bucket c
+    if (c == thr) split_at = run;  // items of cost above thr come before bucket thr
     run += n;
   }
   __syncthreads();
+  // the first ns items appear twice, as halves 0 and 1 (tile | (half + 1) << 24), then the rest
+  const int ns = p.split_cap > 0 ? min(split_at, p.split_cap) : 0;
+  if (tid == 0 && p.nsplit) *p.nsplit = ns;
   for (int b = wave; b < p.batch; b += nwaves) {
     SeqLens L = sched_lens(p, b);
     int nt = (L.own + p.tile_own - 1) / p.tile_own;
     for (int t = lane; t < nt; t += 64) {
-      int pos = atomicAdd(&hist[item_cost(p, L, t)], 1);
-      if (pos < p.max_items) {
-        WorkItem it;
-        it.seq = b;
+      const int pos = atomicAdd(&hist[item_cost(p, L, t)], 1);
+      WorkItem it;
+      it.seq = b;
+      if (pos < ns) {
+        it.tile = t | (1 << 24);
+        p.items[2 * pos] = it;
+        it.tile = t | (2 << 24);
+        p.items[2 * pos + 1] = it;
+      } else if (pos + ns < p.max_items) {
         it.tile = t;
-        p.items[pos] = it;
+        p.items[pos + ns] = it;
       }
     }
   }
-  if (tid == 0) *p.count = min(total, p.max_items);
+  if (tid == 0) *p.count = min(total + ns, p.max_items);
 }
 
 hipError_t launch_schedule(const SchedParams& p, hipStream_t st) {

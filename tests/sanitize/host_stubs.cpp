@@ -23,6 +23,7 @@ bool fwd8_ok(const FwdParams&) { return false; }
 hipError_t launch_bwd(const BwdParams&, DType, hipStream_t) { return hipErrorNotSupported; }
 int bwd_q_tile_rows(const BwdParams&, DType) { return 64; }
 int bwd_k_tile_rows(const BwdParams&, DType) { return 64; }
+int bwd_k_split_cap(const BwdParams&, DType) { return 0; }
 hipError_t launch_merge_fwd(const MergeParams&, DType, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_merge_bwd(const MergeParams&, DType, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_block_mask_build(const BmBuildParams&, hipStream_t) { return hipErrorNotSupported; }

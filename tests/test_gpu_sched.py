@@ -76,3 +76,48 @@ def test_thd_more_than_1024_tiles_sampled():
     assert worst_o <= O_TOL["bf16"] and worst_l <= LSE_TOL
     for n, e in errs.items():
         assert e <= G_TOL["bf16"], f"{n}: {e}"
+
+
+def test_thd_long_dkdv_items_run_in_halves():
+    # seed 3 of the varlen GQA D128 workload: one 3706-token sequence among shorter ones, so
+    # the first key tiles' chains of (q head, q tile) steps exceed the mean per workgroup
+    # slot and run as two half blocks plus a combine; results against the oracle on the
+    # split tiles and elsewhere, and bitwise repeatable
+    w = synth.c4(3)
+    lengths = np.diff(w.cu_seqlens_q).tolist()
+    say(f"case c4 seed 3 lengths {lengths}")
+    q, k, v = to_dev(w)
+    cq, ck = cu_dev(w)
+    g = w.dout.to(DEV)
+    o, lse = gpu_forward(w, q, k, v, cq, ck)
+    runs = [gpu_backward(w, q, k, v, o, lse, g, None, cq, ck) for _ in range(2)]
+    torch.cuda.synchronize()
+    for x, y in zip(*runs):
+        assert torch.equal(x, y)
+    dq, dk, dv = (t.cpu() for t in runs[0])
+    cu = w.cu_seqlens_q
+    s_long = int(np.argmax(lengths))
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    rng = np.random.default_rng(72)
+    for s, kh in [(s_long, 0), (s_long, 3), (int(np.argsort(lengths)[-2]), 1)]:
+        a, b = int(cu[s]), int(cu[s + 1])
+        n = b - a
+        heads = list(range(kh * 4, kh * 4 + 4))
+        ks, vs = (synth.f64(t[a:b, kh]) for t in (w.k, w.v))
+        qh = np.stack([synth.f64(w.q[a:b, h]) for h in heads])
+        gh = np.stack([synth.f64(w.dout[a:b, h]) for h in heads])
+        cols = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 383, 511, n // 2, n - 1],
+                                         rng.integers(0, n, 4)]))
+        rk, rv = oracle.dkdv_cols(qh, ks, vs, gh, w.scale, cols, w.window)
+        got["dk"].append(synth.f64(dk[a + cols, kh]))
+        got["dv"].append(synth.f64(dv[a + cols, kh]))
+        ref["dk"].append(rk)
+        ref["dv"].append(rv)
+        rows = np.unique(np.concatenate([[0, 127, n - 1], rng.integers(0, n, 3)]))
+        got["dq"].append(synth.f64(dq[a + rows, heads[1]]))
+        ref["dq"].append(oracle.dq_rows(qh[1], ks, vs, gh[1], w.scale, rows, w.window))
+    errs = {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= G_TOL["bf16"], f"{n}: {e}"
