@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import scaled_dot_product_05_amd as S
 import synth
 from gpu_util import (DEV, G_TOL, LSE_TOL, O_TOL, check_forward, check_grads, cu_dev, gpu_backward,
                       gpu_bhsd, gpu_forward, oracle_backward, oracle_forward, rel_err, say, to_dev)
@@ -90,8 +91,13 @@ def test_thd_long_dkdv_items_run_in_halves():
     cq, ck = cu_dev(w)
     g = w.dout.to(DEV)
     o, lse = gpu_forward(w, q, k, v, cq, ck)
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(True)
     runs = [gpu_backward(w, q, k, v, o, lse, g, None, cq, ck) for _ in range(2)]
     torch.cuda.synchronize()
+    S.sdpa_profile_enable(False)
+    launched = set(S.sdpa_profile_read())
+    assert {"bwd_dq", "bwd_dkdv", "bwd_dkdv_combine"} <= launched, launched
     for x, y in zip(*runs):
         assert torch.equal(x, y)
     dq, dk, dv = (t.cpu() for t in runs[0])
@@ -117,6 +123,54 @@ def test_thd_long_dkdv_items_run_in_halves():
         rows = np.unique(np.concatenate([[0, 127, n - 1], rng.integers(0, n, 3)]))
         got["dq"].append(synth.f64(dq[a + rows, heads[1]]))
         ref["dq"].append(oracle.dq_rows(qh[1], ks, vs, gh[1], w.scale, rows, w.window))
+    errs = {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= G_TOL["bf16"], f"{n}: {e}"
+
+
+def test_thd_long_dkdv_items_run_in_halves_d64():
+    # head_dim 64 (two dK/dV workgroups per CU): one 6000-token sequence among 120 short
+    # ones, GQA 4/2; its first key tiles run as halves, and the list has over 64 sequences
+    rng = np.random.default_rng(73)
+    lengths = [6000] + rng.integers(100, 301, 120).tolist()
+    w = synth.thd(33, 1300, "bf16", lengths, 4, 2, 64, 0.125, (-1, 0), with_grad=True)
+    say(f"case thd D64 6000 + 120 short, total {sum(lengths)}")
+    q, k, v = to_dev(w)
+    cq, ck = cu_dev(w)
+    g = w.dout.to(DEV)
+    o, lse = gpu_forward(w, q, k, v, cq, ck)
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(True)
+    runs = [gpu_backward(w, q, k, v, o, lse, g, None, cq, ck) for _ in range(2)]
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(False)
+    launched = set(S.sdpa_profile_read())
+    assert {"bwd_dq", "bwd_dkdv", "bwd_dkdv_combine"} <= launched, launched
+    for x, y in zip(*runs):
+        assert torch.equal(x, y)
+    dq, dk, dv = (t.cpu() for t in runs[0])
+    cu = w.cu_seqlens_q
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for s, kh in [(0, 0), (0, 1), (7, 1)]:
+        a, b = int(cu[s]), int(cu[s + 1])
+        n = b - a
+        heads = [2 * kh, 2 * kh + 1]
+        ks, vs = (synth.f64(t[a:b, kh]) for t in (w.k, w.v))
+        qh = np.stack([synth.f64(w.q[a:b, h]) for h in heads])
+        gh = np.stack([synth.f64(w.dout[a:b, h]) for h in heads])
+        cols = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 129, 255, 256, n // 2, n - 1],
+                                         rng.integers(0, n, 3)]))
+        cols = cols[cols < n]
+        rk, rv = oracle.dkdv_cols(qh, ks, vs, gh, w.scale, cols, w.window)
+        got["dk"].append(synth.f64(dk[a + cols, kh]))
+        got["dv"].append(synth.f64(dv[a + cols, kh]))
+        ref["dk"].append(rk)
+        ref["dv"].append(rv)
+        rows = np.unique(np.concatenate([[0, 127, n - 1], rng.integers(0, n, 3)]))
+        got["dq"].append(synth.f64(dq[a + rows, heads[0]]))
+        ref["dq"].append(oracle.dq_rows(qh[0], ks, vs, gh[0], w.scale, rows, w.window))
     errs = {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
     say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
