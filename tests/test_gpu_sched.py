@@ -175,3 +175,49 @@ def test_thd_long_dkdv_items_run_in_halves_d64():
     say("  sampled: " + ", ".join(f"{n} rel err {e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= G_TOL["bf16"], f"{n}: {e}"
+
+
+def test_thd_split_items_accumulate_f16_dlse():
+    # the split path's combine with accumulate=1, fp16 and dLSE: dK, dV added to nonzero
+    # buffers equal the buffers plus the plain result within one fp16 rounding of the sum,
+    # and the plain result matches the oracle on the split key tiles
+    lengths = [290, 3706, 2500, 2006, 1179, 706, 2958, 651]
+    w = synth.thd(34, 1400, "f16", lengths, 16, 4, 128, 128 ** -0.5, (-1, 0), with_grad=True,
+                  with_dlse=True)
+    say("case thd split f16 dLSE accumulate")
+    q, k, v = to_dev(w)
+    cq, ck = cu_dev(w)
+    g, dl = w.dout.to(DEV), w.dlse.to(DEV)
+    o, lse = gpu_forward(w, q, k, v, cq, ck)
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(True)
+    dq, dk, dv = gpu_backward(w, q, k, v, o, lse, g, dl, cq, ck)
+    torch.cuda.synchronize()
+    S.sdpa_profile_enable(False)
+    assert "bwd_dkdv_combine" in set(S.sdpa_profile_read())
+    base_k = (torch.randn(dk.shape, generator=torch.Generator().manual_seed(5)) * 0.01).half().to(DEV)
+    base_v = (torch.randn(dv.shape, generator=torch.Generator().manual_seed(6)) * 0.01).half().to(DEV)
+    base_q = torch.zeros_like(dq)
+    aq, ak, av = gpu_backward(w, q, k, v, o, lse, g, dl, cq, ck, dq=base_q.clone(), dk=base_k.clone(),
+                              dv=base_v.clone(), accumulate=True)
+    torch.cuda.synchronize()
+    for acc, base, plain in ((ak, base_k, dk), (av, base_v, dv), (aq, base_q, dq)):
+        want = base.double() + plain.double()
+        err = float((acc.double() - want).abs().max())
+        assert err <= 2.0 ** -10 * float(want.abs().max()) + 1e-6, err
+    dk, dv = dk.cpu(), dv.cpu()
+    cu = w.cu_seqlens_q
+    s, kh = 1, 2
+    a, b = int(cu[s]), int(cu[s + 1])
+    n = b - a
+    heads = list(range(kh * 4, kh * 4 + 4))
+    ks, vs = (synth.f64(t[a:b, kh]) for t in (w.k, w.v))
+    qh = np.stack([synth.f64(w.q[a:b, h]) for h in heads])
+    gh = np.stack([synth.f64(w.dout[a:b, h]) for h in heads])
+    dlh = np.stack([synth.f64(w.dlse[h, a:b]) for h in heads])
+    cols = np.array([0, 1, 127, 128, 300, 511, 700, n - 1])
+    rk, rv = oracle.dkdv_cols(qh, ks, vs, gh, w.scale, cols, w.window, 0, dlh)
+    ek = rel_err(synth.f64(dk[a + cols, kh]), rk)
+    ev = rel_err(synth.f64(dv[a + cols, kh]), rv)
+    say(f"  sampled: dk rel err {ek:.2e}, dv rel err {ev:.2e}")
+    assert ek <= G_TOL["f16"] and ev <= G_TOL["f16"]
