@@ -20,8 +20,10 @@ LIB = os.path.join(PKG, "libsdpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "profile.cpp", "cp.cpp", "fwd.hip", "bwd.hip", "merge.hip", "sched.hip", "blockmask.hip",
-           "noalloc.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "cp.cpp", "fwd.hip", "bwd.hip", "bwd_dq128.hip", "merge.hip", "sched.hip",
+           "blockmask.hip", "noalloc.hip"]
+# per-source flags: the head_dim-128 dQ kernels take the max-ilp machine scheduler
+EXTRA = {"bwd_dq128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
@@ -29,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                      if "packed-fp32-ops" not in l)

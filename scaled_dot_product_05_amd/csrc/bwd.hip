@@ -2042,6 +2042,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd16w_kernel(BwdParams p) {
 // ----------------------------------------------------------------------------------------
 // launches
 // ----------------------------------------------------------------------------------------
+#ifndef SDPA_BWD_KERNELS_ONLY
+// The separate-launch dQ kernels at head_dim 128 are compiled in bwd_dq128.hip, with a
+// scheduling strategy of their own; this unit only declares them.
+extern template __global__ void bwd_dq16p_kernel<true, 128, 4, true>(BwdParams);
+extern template __global__ void bwd_dq16p_kernel<false, 128, 4, true>(BwdParams);
+
 template <class K>
 static hipError_t go(K kernel, const char* name, int64_t blocks, hipStream_t st, const BwdParams& p,
                      int threads = kThreads) {
@@ -2255,5 +2261,7 @@ hipError_t launch_bwd(const BwdParams& p, DType dt, hipStream_t st) {
       return main32<128>(p, st, bq, bk);
   }
 }
+
+#endif  // SDPA_BWD_KERNELS_ONLY
 
 }  // namespace sdpa
