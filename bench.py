@@ -40,8 +40,8 @@ METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of gfx950 MFMA peak per dt
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8": 5033.2}  # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {  # which source file holds each kernel (for the traffic-staleness check)
-    "attn_fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_pre": "bwd.hip",
+KERNEL_SOURCES = {  # which source files build each kernel (for the traffic-staleness check)
+    "attn_fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": ("bwd.hip", "bwd_dq128.hip"), "bwd_pre": "bwd.hip",
     "bwd_main": "bwd.hip",
     "merge_fwd": "merge.hip", "merge_bwd": "merge.hip", "attn_fwd_short": "fwd.hip",
     "bwd_short": "bwd.hip",
@@ -53,9 +53,12 @@ def log(*a):
 
 
 def source_hash(kernel: str) -> str:
-    path = os.path.join(ROOT, "scaled_dot_product_05_amd", "csrc", KERNEL_SOURCES[kernel])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    files = KERNEL_SOURCES[kernel]
+    h = hashlib.sha256()
+    for name in (files,) if isinstance(files, str) else files:
+        with open(os.path.join(ROOT, "scaled_dot_product_05_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str):
