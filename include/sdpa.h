@@ -246,8 +246,10 @@ int sdpa_fwd_fp8(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_ten
  * of the current device) the fp32 partial dK/dV sums of the two halves of every 64-key block
  * (1 KiB x head_dim per block) and one counter per block, plus for THD on large grids (16-bit,
  * head_dim 64 or 128, no block mask, more than 12 work blocks per compute unit) up to 32 MiB
- * of fp32 partial dK/dV sums for the longest key tiles, which may run as two halves.  Host
- * only; query it with the device that will run the call current. */
+ * of fp32 partial dK/dV sums for the longest key tiles, which may run as two halves.  That
+ * last room is optional: given a workspace without it, sdpa_bwd splits no key tile (the
+ * results then differ only in the order of their fp32 sums).  Host only; query it with the
+ * device that will run the call current. */
 int sdpa_bwd_workspace_size(const sdpa_desc_t* desc, size_t* bytes);
 
 /* Host-only dry run of sdpa_bwd's validation. */
@@ -275,8 +277,8 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
  * tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the workspace
  * taken from a static device buffer of sdpa_bwd_noalloc_max_workspace() bytes (64 MiB) that
  * each GPU holds until the process ends, instead of the caller's.  Arguments, results and
- * errors as sdpa_bwd; a problem whose sdpa_bwd_workspace_size exceeds the buffer returns
- * ERR_WORKSPACE before anything runs.  Allocates nothing (no hipMalloc / hipFree).  Every
+ * errors as sdpa_bwd; a problem whose workspace, less the optional room for split key tiles,
+ * exceeds the buffer returns ERR_WORKSPACE before anything runs.  Allocates nothing (no hipMalloc / hipFree).  Every
  * call on one GPU shares that GPU's buffer: calls that overlap on one GPU (other streams or
  * host threads) race and must be serialised by the caller; calls on one stream are ordered.
  * The buffer needs no clearing: each call's kernels write what they later read. */

@@ -425,13 +425,15 @@ int64_t bwd_ksplit_cap(const Shape& s, int32_t dtype) {
   return std::max<int64_t>(1, std::min<int64_t>(64, (int64_t(32) << 20) / per));
 }
 
-BwdWs bwd_ws_layout(const Shape& s, int32_t dtype) {
+// split_area = false: the layout without room for split THD dK/dV items (the backward then
+// splits none); a workspace of at least that size still runs.
+BwdWs bwd_ws_layout(const Shape& s, int32_t dtype, bool split_area = true) {
   BwdWs w{};
   int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
   w.delta_off = 0;
   w.lse2_off = round_up(rows * 4, 256);
   int64_t off = round_up(w.lse2_off + rows * 4, 256);
-  w.ksplit_cap = bwd_ksplit_cap(s, dtype);
+  w.ksplit_cap = split_area ? bwd_ksplit_cap(s, dtype) : 0;
   if (s.thd) {
     w.wq_off = off;
     off = round_up(off + thd_items(s.total_q, s.batch, bwd_q_rows(dtype)) * int64_t(sizeof(WorkItem)), 256);
@@ -545,6 +547,7 @@ int bwd_check(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor
   Norm ins[7] = {nq, nk, nv, no, ndo, nl, ndl};
   if ((rc = check_outputs(outs, 3, ins, has_dlse ? 7 : 6))) return rc;
   BwdWs w = bwd_ws_layout(a->s, a->dtype);
+  if (ws_bytes < size_t(w.total)) w = bwd_ws_layout(a->s, a->dtype, false);  // no split room
   if (ws_bytes < size_t(w.total))
     return fail(SDPA_ERR_WORKSPACE, "workspace %zu bytes, %lld needed", ws_bytes, (long long)w.total);
   memset(p, 0, sizeof(*p));
@@ -738,6 +741,15 @@ int device_cus() {
 
 // Record an error message for sdpa_last_error() from another translation unit.
 int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+// The smallest backward workspace for desc: without room for split THD dK/dV items.
+int bwd_workspace_min(const sdpa_desc_t* desc, size_t* bytes) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  *bytes = size_t(bwd_ws_layout(s, desc->dtype, false).total);
+  return ok();
+}
 int clear_error() { return ok(); }
 }  // namespace sdpa
 
@@ -871,6 +883,7 @@ int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_
   if (rc) return rc;
   if (accumulate != 0 && accumulate != 1) return fail(SDPA_ERR_ARG, "accumulate must be 0 or 1");
   BwdWs w = bwd_ws_layout(a.s, a.dtype);
+  if (workspace_bytes < size_t(w.total)) w = bwd_ws_layout(a.s, a.dtype, false);  // as bwd_check
   if (w.total > 0 && !workspace) return fail(SDPA_ERR_WORKSPACE, "backward needs a workspace");
   debug_log("bwd", a, &p.aligned);
   if (a.s.batch == 0 || (a.rows_q == 0 && a.rows_k == 0)) return ok();

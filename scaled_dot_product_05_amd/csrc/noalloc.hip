@@ -21,6 +21,7 @@
 
 namespace sdpa {
 int set_error(int code, const char* msg);
+int bwd_workspace_min(const sdpa_desc_t* desc, size_t* bytes);
 }
 
 namespace {
@@ -64,8 +65,10 @@ int sdpa_bwd_noalloc(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa
                      const sdpa_tensor_t* dout, const sdpa_rowstat_t* dlse,
                      const sdpa_tensor_t* dq, const sdpa_tensor_t* dk, const sdpa_tensor_t* dv,
                      int accumulate, void* stream) {
+  // the smallest workspace the backward runs with (room for split THD dK/dV items is used
+  // only when the buffer holds it too)
   size_t need = 0;
-  int rc = sdpa_bwd_workspace_size(desc, &need);
+  int rc = sdpa::bwd_workspace_min(desc, &need);
   if (rc) return rc;
   if (need > kScratchBytes) {
     char msg[256];

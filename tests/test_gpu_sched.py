@@ -221,3 +221,36 @@ def test_thd_split_items_accumulate_f16_dlse():
     ev = rel_err(synth.f64(dv[a + cols, kh]), rv)
     say(f"  sampled: dk rel err {ek:.2e}, dv rel err {ev:.2e}")
     assert ek <= G_TOL["f16"] and ev <= G_TOL["f16"]
+
+
+def test_thd_split_room_in_the_workspace_is_optional():
+    # a workspace one byte short of sdpa_bwd_workspace_size lacks the room for split items:
+    # the same call then splits nothing (no combine launch), dQ is bitwise the same and dK, dV
+    # differ only by the order of their fp32 sums
+    w = synth.c4(3)
+    q, k, v = to_dev(w)
+    g = w.dout.to(DEV)
+    kw = dict(cu_seqlens_q=torch.from_numpy(w.cu_seqlens_q).to(DEV),
+              max_seqlen_q=int(np.diff(w.cu_seqlens_q).max()))
+    o, lse = S.forward(q, k, v, w.layout, w.scale, w.window, **kw)
+    pr = S.Problem(q, k, w.layout, w.scale, w.window, **kw)
+    full = S.sdpa_bwd_workspace_size(pr.desc)
+    say(f"case c4 seed 3 workspace {full} and {full - 1} bytes")
+
+    def run(nbytes):
+        grads = tuple(torch.empty_like(t) for t in (q, k, v))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        torch.cuda.synchronize()
+        S.sdpa_profile_enable(True)
+        S.sdpa_bwd(pr.desc, q, k, v, o, lse, g, None, *grads, False, ws)
+        torch.cuda.synchronize()
+        S.sdpa_profile_enable(False)
+        return grads, set(S.sdpa_profile_read())
+
+    (dq1, dk1, dv1), l1 = run(full)
+    (dq2, dk2, dv2), l2 = run(full - 1)
+    assert "bwd_dkdv_combine" in l1 and "bwd_dkdv_combine" not in l2, (l1, l2)
+    assert torch.equal(dq1, dq2)
+    for a, b in ((dk1, dk2), (dv1, dv2)):
+        a, b = a.double(), b.double()
+        assert float((a - b).abs().max()) <= 2.0 ** -7 * float(b.abs().max())
