@@ -254,3 +254,38 @@ def test_thd_split_room_in_the_workspace_is_optional():
     for a, b in ((dk1, dk2), (dv1, dv2)):
         a, b = a.double(), b.double()
         assert float((a - b).abs().max()) <= 2.0 ** -7 * float(b.abs().max())
+
+
+@pytest.mark.parametrize("seed,hq,hk,d", [(80, 16, 4, 128), (81, 8, 2, 64), (82, 16, 16, 128),
+                                          (83, 8, 1, 64)])
+def test_thd_split_equals_unsplit_on_skewed_mixes(seed, hq, hk, d):
+    # seeded length mixes with one long sequence: the backward with the split room (items
+    # above the mean may run as halves) against the same call without it (no split); dQ is
+    # bitwise the same, dK and dV differ only by the order of their fp32 sums
+    rng = np.random.default_rng(seed)
+    lengths = [int(rng.integers(3000, 6001))] + rng.integers(1, 1500, int(rng.integers(30, 60))).tolist()
+    w = synth.thd(seed, 1500, "bf16", lengths, hq, hk, d, d ** -0.5, (-1, 0), with_grad=True)
+    q, k, v = to_dev(w)
+    g = w.dout.to(DEV)
+    kw = dict(cu_seqlens_q=torch.from_numpy(w.cu_seqlens_q).to(DEV), max_seqlen_q=max(lengths))
+    o, lse = S.forward(q, k, v, w.layout, w.scale, w.window, **kw)
+    pr = S.Problem(q, k, w.layout, w.scale, w.window, **kw)
+    full = S.sdpa_bwd_workspace_size(pr.desc)
+    out = []
+    for nbytes in (full, full - 1):
+        grads = tuple(torch.empty_like(t) for t in (q, k, v))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        S.sdpa_profile_enable(True)
+        S.sdpa_bwd(pr.desc, q, k, v, o, lse, g, None, *grads, False, ws)
+        torch.cuda.synchronize()
+        S.sdpa_profile_enable(False)
+        out.append((grads, set(S.sdpa_profile_read())))
+    (dq1, dk1, dv1), l1 = out[0]
+    (dq2, dk2, dv2), l2 = out[1]
+    say(f"case seed {seed} H{hq}/{hk} D{d} {len(lengths)} sequences, total {sum(lengths)}: "
+        f"combine {'bwd_dkdv_combine' in l1}")
+    assert "bwd_dkdv_combine" not in l2
+    assert torch.equal(dq1, dq2)
+    for a, b in ((dk1, dk2), (dv1, dv2)):
+        a, b = a.double(), b.double()
+        assert float((a - b).abs().max()) <= 2.0 ** -7 * float(b.abs().max())
