@@ -263,9 +263,11 @@ int sdpa_bwd_validate(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdp
  * returned LSE).  Reads q, k, v, o, lse (from sdpa_fwd), dout and optionally dlse
  * (dlse == NULL or dlse->data == NULL means dL/dLSE = 0).  Writes dq (q's shape), dk and dv
  * (k's shape; summed over the q heads of each group).  No atomic accumulation: every output
- * element has one writer (under GQA the second of a block's two halves to finish, found with
- * one atomic counter per block, adds the first half's partial sums in fp32; the result does
- * not depend on which half finishes first).  accumulate = 0 overwrites, 1 adds to the existing contents (to sum the
+ * element has one writer (under GQA on small grids the second of a block's two halves to
+ * finish, found with one atomic counter per block, adds the first half's partial sums in
+ * fp32; under THD on large grids the two halves of a long key tile write their fp32 sums to
+ * slots of their own and a following launch adds them; neither result depends on which half
+ * finishes first).  accumulate = 0 overwrites, 1 adds to the existing contents (to sum the
  * gradients of several partial attentions into one buffer). */
 int sdpa_bwd(const sdpa_desc_t* desc, const sdpa_tensor_t* q, const sdpa_tensor_t* k,
              const sdpa_tensor_t* v, const sdpa_tensor_t* o, const sdpa_rowstat_t* lse,
