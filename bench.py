@@ -498,6 +498,10 @@ def extra(torch, S, synth, dev):
     res["f32_causal_fwd_bwd"] = fwd_bwd_split(torch, S, synth.target(b=4, s=4096, with_grad=True,
                                                                       dtype="f32"), dev)
 
+    # context-parallel ring emulated on one GPU (TE 885): 2 cp load-balanced chunks, per-hop
+    # forward/backward over (q chunk, kv chunk) pairs folded with the LSE merge, against the
+    # plain call on the same inputs
+    res["cp_ring_emulated_bf16"] = cp_ring(torch, S, synth, dev)
     res["block_sparse_bf16"] = block_sparse(torch, S, synth, dev)
     res["fp8_e4m3_fwd"] = fp8_forward(torch, S, synth, dev)
 
@@ -538,6 +542,33 @@ def extra(torch, S, synth, dev):
         del q, k, v, o, lse, g, dq, dk, dv
     res["short_seq_fwd_bf16"] = ss
     return res
+
+
+def cp_ring(torch, S, synth, dev):
+    """Causal B2 S16384 H8 D64 bf16 fwd+bwd: plain calls, and the ring emulated at cp 2 and 4
+    (the same algorithmic flops, 14 D per visible pair)."""
+    w = synth.target(b=2, s=16384, with_grad=True)
+    q, k, v, g = (t.to(dev) for t in (w.q, w.k, w.v, w.dout))
+    flops = 14 * 64 * (2 * 8 * 16384 * 16385 // 2)
+
+    def plain():
+        o, lse = S.forward(q, k, v, "bshd", w.scale, (-1, 0))
+        S.backward(q, k, v, o, lse, g, "bshd", w.scale, (-1, 0))
+
+    ms = time_calls(torch, plain)
+    out = {"B": 2, "S": 16384, "H": 8, "D": 64, "plain_ms": round(ms, 4),
+           "plain_TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2)}
+    for cp in (2, 4):
+        def ring():
+            o, lse = S.cp_forward(q, k, v, "bshd", w.scale, (-1, 0), cp)
+            S.cp_backward(q, k, v, o, lse, g, "bshd", w.scale, (-1, 0), cp)
+
+        ms = time_calls(torch, ring)
+        out[f"cp{cp}_ms"] = round(ms, 4)
+        out[f"cp{cp}_TFLOP/s"] = round(flops / (ms * 1e-3) / 1e12, 2)
+        log(f"cp ring cp={cp}: {ms:.3f} ms (plain {out['plain_ms']:.3f} ms)")
+    del q, k, v, g
+    return out
 
 
 def fwd_bwd_split(torch, S, w, dev):
