@@ -252,7 +252,8 @@ def main() -> int:
 
     wl = args.workload
     fwd_only = wl in ("target", "target_d128")
-    w = {"c4": lambda: synth.c4(), "c2": lambda: synth.c2(), "target": lambda: synth.target(),
+    w = {"c4": lambda: synth.c4(), "c4_seed3": lambda: synth.c4(3), "c2": lambda: synth.c2(),
+         "target": lambda: synth.target(),
          "target_d128": lambda: synth.target(h=16, d=128),
          "target_step": lambda: synth.target(with_grad=True),
          "f32_step": lambda: synth.target(b=4, s=4096, with_grad=True, dtype="f32")}[wl]()
@@ -342,6 +343,9 @@ MFMA_WORKLOADS = {
     "c4": ("varlen THD causal self-attention fwd+bwd, bf16: 8 sequences with lengths uniform on "
            "[256,4096] (seed 0), int32 cu_seqlens, 16 q heads, 4 kv heads (GQA), head_dim 128, "
            "scale 1/sqrt(128), N(0,1) q, k, v, dO"),
+    "c4_seed3": ("the same varlen THD GQA D128 fwd+bwd with the lengths of seed 3 (290, 3706, 2500, "
+                 "2006, 1179, 706, 2958, 651): one dominant sequence, whose first key tiles the "
+                 "backward splits in halves"),
     "c2": ("causal self-attention fwd+bwd, bf16, B4 S1024 H8 D64, BSHD contiguous, scale 1/8, "
            "N(0,1) inputs"),
     "target": ("causal self-attention forward, bf16, B8 S4096 H8 D64, BSHD contiguous, scale 1/8, "
