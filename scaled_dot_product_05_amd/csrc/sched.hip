@@ -59,7 +59,7 @@ struct SchedPair {
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedPair pp) {
   const SchedParams& p = pp.p[blockIdx.x];
   __shared__ int hist[kSchedBuckets];
-  __shared__ int part[kSchedThreads];
+  __shared__ int part[2 * (kSchedThreads / 64) + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int nwaves = kSchedThreads / 64;
   constexpr int PER = kSchedBuckets / kSchedThreads;
@@ -105,20 +105,30 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedPair pp) {
     thr = int64_t(total_cost) * p.split_heads / p.split_slots;
     if (int64_t(max_cost) * 10 <= thr * 15) thr = kSchedBuckets;
   }
-  // exclusive scan in decreasing cost order: thread i owns reversed buckets PER*i .. PER*i+PER-1
+  // exclusive scan in decreasing cost order: thread i owns reversed buckets PER*i .. PER*i+PER-1;
+  // an inclusive scan inside each wave, then one over the wave totals in wave 0
   int local = 0;
   for (int k = 0; k < PER; ++k) local += hist[kSchedBuckets - 1 - (PER * tid + k)];
-  part[tid] = local;
-  __syncthreads();
-  for (int step = 1; step < kSchedThreads; step <<= 1) {
-    int v = tid >= step ? part[tid - step] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int incl = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
   }
-  int run = part[tid] - local;  // exclusive prefix of this thread's first bucket
-  const int total = part[kSchedThreads - 1];
+  if (lane == 63) part[wave] = incl;
   __syncthreads();
+  if (wave == 0) {
+    const int t = lane < nwaves ? part[lane] : 0;
+    int x = t;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane < nwaves) part[nwaves + lane] = x - t;  // items before wave `lane`
+    if (lane == nwaves - 1) part[2 * nwaves] = x;
+  }
+  __syncthreads();
+  int run = part[nwaves + wave] + incl - local;  // exclusive prefix of this thread's first bucket
+  const int total = part[2 * nwaves];
   for (int k = 0; k < PER; ++k) {
     int c = kSchedBuckets - 1 - (PER * tid + k);
     int n = hist[c];
