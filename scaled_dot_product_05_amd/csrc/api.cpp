@@ -326,6 +326,22 @@ int check_desc(const sdpa_desc_t* d, Shape* s) {
   }
   s->scale = d->softmax_scale;
   s->scale_log2 = float(double(d->softmax_scale) * 1.4426950408889634);
+  {
+    // The tile kernels launch at most 4 work-items per query and per key row, rows padded to
+    // 128-row tiles per (sequence, head), and a dispatch counts work-items in 32 bits: refuse
+    // here what no grid could cover, before any launch (double: the products of extreme
+    // descriptor values overflow 64 bits)
+    auto padded = [&](double rows, double heads) {
+      return thd ? heads * (rows + double(d->batch) * 128)
+                 : heads * double(d->batch) * ceil(rows / 128) * 128;
+    };
+    const double pq = padded(thd ? double(d->total_q) : double(d->seqlen_q), d->heads_q);
+    const double pk = padded(thd ? double(d->total_k) : double(d->seqlen_k), d->heads_kv);
+    if (4 * (pq + pk) > double(kMaxGridItems))
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "problem too large: %.0f padded query and key rows over all heads, at most %lld",
+                  pq + pk, (long long)(kMaxGridItems / 4));
+  }
   return SDPA_OK;
 }
 

@@ -96,6 +96,8 @@ __global__ __launch_bounds__(256) void bm_cols_kernel(BmBuildParams p) {
 }
 
 hipError_t launch_block_mask_build(const BmBuildParams& p, hipStream_t st) {
+  if (!grid_fits(int64_t(p.planes) * p.nqb, 256) || !grid_fits(int64_t(p.planes) * p.nkb, 256))
+    return hipErrorInvalidConfiguration;
   prof_begin(st, "mask_rows");
   hipLaunchKernelGGL(bm_rows_kernel, dim3(unsigned(p.planes * p.nqb)), dim3(256), 0, st, p);
   prof_end(st);

@@ -43,12 +43,10 @@ __device__ __forceinline__ int64_t delta_index(const Shape& s, int b, int h, con
 // pre-pass: Delta_i = dO_i . O_i - dLSE_i, and LSE_i log2(e) as a contiguous array
 // ----------------------------------------------------------------------------------------
 template <int ES, bool BF, int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
-  constexpr int VPT = 16 / ES, TPR = D / VPT, RPB = kThreads / TPR;
+__device__ __forceinline__ void bwd_pre_rows(const BwdParams& p, int64_t rows, int64_t r) {
+  constexpr int VPT = 16 / ES, TPR = D / VPT;
   const Shape& s = p.s;
   const int tid = threadIdx.x;
-  const int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
-  const int64_t r = int64_t(blockIdx.x) * RPB + tid / TPR;
   const bool live = r < rows;
   int64_t b = 0, h, t;
   if (s.thd) {
@@ -59,11 +57,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
     int64_t bh = live ? r / s.sq : 0;
     h = bh % s.hq;
     b = bh / s.hq;
-  }
-  if (p.nsplit > 1) {
-    // counters of the split dK/dV blocks of the launch that follows on this stream
-    for (int64_t i = int64_t(blockIdx.x) * kThreads + tid; i < p.split_blocks; i += int64_t(gridDim.x) * kThreads)
-      p.split_cnt[i] = 0;
   }
   const int c = (tid % TPR) * VPT;
   float dot = 0.f;
@@ -92,6 +85,23 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
     const float l = p.lse.ptr[b * p.lse.sb + h * p.lse.sh + t * p.lse.ss];
     p.lse2[r] = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
+}
+
+// RPB rows per workgroup per pass; the grid is capped and loops over the rest, with the same
+// row group across the workgroup in every pass (the row reduction needs all its lanes)
+template <int ES, bool BF, int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
+  constexpr int TPR = D / (16 / ES), RPB = kThreads / TPR;
+  const Shape& s = p.s;
+  const int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
+  if (p.nsplit > 1) {
+    // counters of the split dK/dV blocks of the launch that follows on this stream
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < p.split_blocks;
+         i += int64_t(gridDim.x) * kThreads)
+      p.split_cnt[i] = 0;
+  }
+  for (int64_t r0 = int64_t(blockIdx.x) * RPB; r0 < rows; r0 += int64_t(gridDim.x) * RPB)
+    bwd_pre_rows<ES, BF, D>(p, rows, r0 + threadIdx.x / TPR);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1415,7 +1425,8 @@ __device__ __forceinline__ void dkdv16p_body(const BwdParams& p, lds_t* const ld
     qoff[u] = uint32_t(row * qss * 2 + ((pos ^ swb<CPR>(row)) * 16));
     goff[u] = uint32_t(row * gss * 2 + ((pos ^ swb<CPR>(row)) * 16));
   }
-  // wave 0 loads the tile rows' LSE log2e, wave 1 their Delta (lanes 0..31)
+  // wave 0 loads the tile rows' LSE log2e, wave 1 their Delta (lanes 0..31); the host keeps
+  // the whole array below 2^31 bytes for this kernel
   const i32x4_t rstat = make_rsrc(wave == 0 ? p.lse2 : p.delta, p.ws_rows * 4);
   auto issue_at = [&](int gi, int qt, bool part, int slot) {
     const int h = hk * s.group + gi, qbase = qt * BQ;
@@ -2052,6 +2063,7 @@ template <class K>
 static hipError_t go(K kernel, const char* name, int64_t blocks, hipStream_t st, const BwdParams& p,
                      int threads = kThreads) {
   if (blocks <= 0) return hipSuccess;
+  if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;
   prof_begin(st, name);
   hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(threads), 0, st, p);
   prof_end(st);
@@ -2068,6 +2080,17 @@ static bool pipelined_ok(const BwdParams& p, int64_t rows, int64_t ss_a, int64_t
          (rows + 4 * 64) * ss * 2 < (int64_t(1) << 31);
 }
 
+// The pipelined dK/dV kernels: the streamed Q/dO rows as above, and LSE log2(e) and Delta read
+// through one buffer resource over the whole workspace array (one fp32 per q head and row), so
+// that array must stay below 2^31 bytes; larger problems take the kernels with 64-bit
+// addressing
+template <int D>
+static bool kv_pipelined(const BwdParams& p) {
+  const int64_t rows = int64_t(p.s.hq) * (p.s.thd ? p.s.total_q : int64_t(p.s.batch) * p.s.sq);
+  return pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV) &&
+         rows * 4 < (int64_t(1) << 31);
+}
+
 // head_dim 64 or 128, 16-bit, both pipelined kernels usable, no block mask, no dK/dV split
 // and a large grid: dQ and dK/dV run as two launches of four-wave workgroups (at D128 the dQ
 // half then runs two waves per SIMD instead of the dK/dV body's one; both halves share each
@@ -2078,8 +2101,7 @@ static bool pipelined_ok(const BwdParams& p, int64_t rows, int64_t ss_a, int64_t
 // separate launch took 495 -> 871 us (each half's release of its partial sums).
 template <int D>
 static bool dq_wide_d(const BwdParams& p) {
-  return pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV) &&
-         pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ) &&
+  return kv_pipelined<D>(p) && pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ) &&
          (p.aligned & kAlO) && p.o.ss >= D;
 }
 // The two launches pay off once the fused launch would have more than kBwdWideMinPerCU
@@ -2130,7 +2152,8 @@ static hipError_t pre(const BwdParams& p, hipStream_t st) {
   int64_t rows = s.thd ? int64_t(s.hq) * s.total_q : int64_t(s.batch) * s.hq * s.sq;
   auto launch = [&](auto kernel, int d) {
     int rpb = kThreads / (d / (16 / ES));
-    const int64_t blocks = (rows + rpb - 1) / rpb;
+    int64_t blocks = (rows + rpb - 1) / rpb;
+    if (blocks > kMaxRowBlocks) blocks = kMaxRowBlocks;
     return go(kernel, "bwd_pre", p.nsplit > 1 && blocks < 1 ? 1 : blocks, st, p);  // it zeroes the split counters
   };
   if (s.d == 32) return launch(bwd_pre_kernel<ES, BF, 32>, 32);
@@ -2142,7 +2165,7 @@ template <bool BF, int D>
 static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t bk) {
   if constexpr (D >= 64) {
     static_assert(kBwdQ16 == 64 && kBwdK16 == 64, "tile rows of the pipelined kernels");
-    const bool kv = pipelined_ok<D>(p, p.s.sq, p.q.ss, p.dout.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV);
+    const bool kv = kv_pipelined<D>(p);
     const bool q = pipelined_ok<D>(p, p.s.sk, p.k.ss, p.v.ss, kAlQ | kAlK | kAlV | kAlDO | kAlDQ);
     if constexpr (D == 128 || D == 64) {
       if (dq_wide(p, BF ? DType::BF16 : DType::F16)) {
@@ -2162,7 +2185,7 @@ static hipError_t main16(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
       if (bk + bq <= 0) return hipSuccess;
       const bool split = !p.s.bm.bits && p.nsplit == 2 && bk == p.split_blocks;
       const int64_t grid = bk * (split ? 2 : 1) + bq;
-      if (grid > 0x7fffffff) return hipErrorInvalidValue;
+      if (!grid_fits(grid, 128)) return hipErrorInvalidConfiguration;
       prof_begin(st, "bwd_main");
       if (p.s.bm.bits)
         hipLaunchKernelGGL((bwd_fused16p_kernel<BF, D, 2, true, false>), dim3(unsigned(grid)), dim3(128), 0, st, p, int(bk));
@@ -2202,10 +2225,8 @@ static hipError_t main32(const BwdParams& p, hipStream_t st, int64_t bq, int64_t
 bool bwd_block_mask_ok(const BwdParams& p, DType dt) {
   if (dt == DType::F32) return true;
   if (p.s.d < 64) return false;
-  constexpr int32_t need_kv = kAlQ | kAlK | kAlV | kAlDO | kAlDK | kAlDV;
   constexpr int32_t need_q = kAlQ | kAlK | kAlV | kAlDO | kAlDQ;
-  const bool kv = p.s.d == 64 ? pipelined_ok<64>(p, p.s.sq, p.q.ss, p.dout.ss, need_kv)
-                              : pipelined_ok<128>(p, p.s.sq, p.q.ss, p.dout.ss, need_kv);
+  const bool kv = p.s.d == 64 ? kv_pipelined<64>(p) : kv_pipelined<128>(p);
   const bool q = p.s.d == 64 ? pipelined_ok<64>(p, p.s.sk, p.k.ss, p.v.ss, need_q)
                              : pipelined_ok<128>(p, p.s.sk, p.k.ss, p.v.ss, need_q);
   // per-head masks stage every head's column list of a key block in LDS
@@ -2225,7 +2246,7 @@ template <bool BF>
 static hipError_t go_bwd_short(const BwdParams& p, hipStream_t st) {
   const int64_t blocks = (int64_t(p.s.batch) * p.s.hk + kWaves - 1) / kWaves;
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   prof_begin(st, "bwd_short");
   if (p.s.d == 32)
     hipLaunchKernelGGL((bwd16w_kernel<BF, 32>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);

@@ -1230,6 +1230,7 @@ static int64_t fwd_grid(const FwdParams& p, int rows) {
 
 template <class K>
 static hipError_t go(K kernel, int blocks, hipStream_t st, const FwdParams& p) {
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   prof_begin(st, "attn_fwd");
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, st, p);
   prof_end(st);
@@ -1260,7 +1261,7 @@ static hipError_t go_short(const FwdParams& p, hipStream_t st) {
   const int64_t items = int64_t(p.s.batch) * p.s.hq * ((p.s.sq + 31) / 32);
   const int64_t blocks = (items + kWaves - 1) / kWaves;
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   prof_begin(st, "attn_fwd_short");
   hipLaunchKernelGGL((fwd16w_kernel<BF, D>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
   prof_end(st);
@@ -1274,7 +1275,7 @@ static hipError_t go16(const FwdParams& p, hipStream_t st) {
   static_assert(BM == kFwdBM16, "host and kernel tile rows differ");
   const int64_t blocks = fwd_grid(p, BM);
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   const bool al = (p.aligned & (kAlQ | kAlK | kAlV | kAlO)) == (kAlQ | kAlK | kAlV | kAlO);
   if (fwd_pipelined(p)) {
     if (p.s.bm.bits) return go(fwd16p_kernel<BF, D, MINB, 1, kFwdBNP, true>, int(blocks), st, p);
@@ -1588,7 +1589,7 @@ bool fwd8_ok(const FwdParams& p) {
 hipError_t launch_fwd8(const FwdParams& p, hipStream_t st) {
   const int64_t blocks = fwd_grid(p, 32 * kWaves);
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   prof_begin(st, "attn_fwd_fp8");
   if (p.s.d == 64)
     hipLaunchKernelGGL(fwd8_kernel<64>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
@@ -1604,7 +1605,7 @@ hipError_t launch_fwd(const FwdParams& p, DType dt, hipStream_t st) {
   if (dt == DType::F16) return fwd16_dispatch<false>(p, st);
   const int64_t blocks = fwd_grid(p, kFwdBM);
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   if (s.bm.bits) {
     if (s.d == 32) return go(fwd32_kernel<32, true>, int(blocks), st, p);
     if (s.d == 64) return go(fwd32_kernel<64, true>, int(blocks), st, p);

@@ -6,6 +6,15 @@
 
 namespace sdpa {
 
+// A dispatch carries its grid size in work-items as a 32-bit value, so blocks x threads must
+// stay below 2^32 (a larger grid would be cut short, not refused).
+constexpr int64_t kMaxGridItems = 0xffffffffLL;
+inline bool grid_fits(int64_t blocks, int threads) {
+  return blocks >= 0 && threads > 0 && blocks <= kMaxGridItems / threads;
+}
+// Grids of the kernels that take a few rows per workgroup and loop over the rest.
+constexpr int64_t kMaxRowBlocks = int64_t(1) << 20;
+
 hipError_t launch_schedule(const SchedParams& p, hipStream_t stream);
 // two lists in one launch (one workgroup each)
 hipError_t launch_schedule2(const SchedParams& a, const SchedParams& b, hipStream_t stream);

@@ -108,10 +108,9 @@ __device__ __forceinline__ void weights(float la, float lb, float& alpha, float&
 }
 
 template <int ES, bool BF, int D>
-__global__ __launch_bounds__(kThreads) void merge_fwd_kernel(MergeParams p) {
+__device__ __forceinline__ void merge_fwd_row(const MergeParams& p, int64_t r) {
   using M = RowMap<ES, D>;
   const int tid = threadIdx.x;
-  const int64_t r = int64_t(blockIdx.x) * M::RPB + tid / M::TPR;
   if (r >= p.rows) return;
   const int c = (tid % M::TPR) * M::VPT;
   const RowPos q = row_pos(p, r);
@@ -128,10 +127,9 @@ __global__ __launch_bounds__(kThreads) void merge_fwd_kernel(MergeParams p) {
 }
 
 template <int ES, bool BF, int D>
-__global__ __launch_bounds__(kThreads) void merge_bwd_kernel(MergeParams p) {
+__device__ __forceinline__ void merge_bwd_row(const MergeParams& p, int64_t r) {
   using M = RowMap<ES, D>;
   const int tid = threadIdx.x;
-  const int64_t r = int64_t(blockIdx.x) * M::RPB + tid / M::TPR;
   const int c = (tid % M::TPR) * M::VPT;
   const RowPos q = row_pos(p, r < p.rows ? r : 0);
   const bool live = r < p.rows && q.s >= 0;  // every lane takes part in the row reduction below
@@ -162,10 +160,33 @@ __global__ __launch_bounds__(kThreads) void merge_bwd_kernel(MergeParams p) {
   }
 }
 
+// RPB rows per workgroup; a grid capped at kMaxRowBlocks loops over the rest, with the same
+// row group across the workgroup in every pass (the backward's row reduction needs all its
+// lanes)
+template <int ES, bool BF, int D>
+__global__ __launch_bounds__(kThreads) void merge_fwd_kernel(MergeParams p) {
+  using M = RowMap<ES, D>;
+  const int64_t r0 = int64_t(blockIdx.x) * M::RPB, step = int64_t(gridDim.x) * M::RPB;
+  merge_fwd_row<ES, BF, D>(p, r0 + threadIdx.x / M::TPR);
+  if (gridDim.x == kMaxRowBlocks)
+    for (int64_t r = r0 + step; r < p.rows; r += step) merge_fwd_row<ES, BF, D>(p, r + threadIdx.x / M::TPR);
+}
+
+template <int ES, bool BF, int D>
+__global__ __launch_bounds__(kThreads) void merge_bwd_kernel(MergeParams p) {
+  using M = RowMap<ES, D>;
+  const int64_t r0 = int64_t(blockIdx.x) * M::RPB, step = int64_t(gridDim.x) * M::RPB;
+  merge_bwd_row<ES, BF, D>(p, r0 + threadIdx.x / M::TPR);
+  if (gridDim.x == kMaxRowBlocks)
+    for (int64_t r = r0 + step; r < p.rows; r += step) merge_bwd_row<ES, BF, D>(p, r + threadIdx.x / M::TPR);
+}
+
 template <template <int, bool, int> class K, int ES, bool BF>
 static hipError_t merge_go(const MergeParams& p, hipStream_t st, bool fwd) {
   auto pick = [&](auto kernel, int rpb) {
     int64_t blocks = (p.rows + rpb - 1) / rpb;
+    if (blocks > kMaxRowBlocks) blocks = kMaxRowBlocks;
+    if (blocks <= 0) return hipSuccess;
     prof_begin(st, fwd ? "merge_fwd" : "merge_bwd");
     hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, p);
     prof_end(st);

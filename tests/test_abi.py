@@ -116,6 +116,28 @@ def test_workspace_sizes_and_checks():
     assert S.sdpa_bwd_workspace_size(dense) >= 2 * 4 * 50 * 4
 
 
+def test_grids_beyond_32bit_work_items_are_refused():
+    # A dispatch counts its work-items in 32 bits and the tile kernels launch at most 4 per
+    # query and per key row (rows padded to 128 per sequence and head): with 64 heads, 2^23
+    # query and key rows each is the first size refused, dense and THD alike.
+    ok = S.make_desc("bshd", "bf16", 1, 2 ** 23 - 128, 2 ** 23 - 128, 64, 64, 64, 0.125)
+    assert S.sdpa_bwd_workspace_size(ok) >= 2 * 4 * 64 * (2 ** 23 - 128)
+    assert S.sdpa_fwd_workspace_size(ok) == 0
+    for fn in (S.sdpa_fwd_workspace_size, S.sdpa_bwd_workspace_size):
+        with pytest.raises(S.SdpaError) as e:
+            fn(S.make_desc("bshd", "bf16", 1, 2 ** 23, 2 ** 23, 64, 64, 64, 0.125))
+        assert e.value.name == "ERR_UNSUPPORTED" and "too large" in str(e.value)
+    cu = torch.tensor([0, 40, 100], dtype=torch.int32)
+    rows = 2 ** 23 - 2 * 128 - 1  # THD: each of 2 sequences may add a partial tile
+    thd_ok = S.make_desc("thd", "bf16", 2, 60, 60, 64, 64, 64, 0.125, cu_seqlens_q=cu,
+                         total_q=rows, total_k=rows)
+    assert S.sdpa_fwd_workspace_size(thd_ok) > 0
+    with pytest.raises(S.SdpaError) as e:
+        S.sdpa_fwd_workspace_size(S.make_desc("thd", "bf16", 2, 60, 60, 64, 64, 64, 0.125,
+                                              cu_seqlens_q=cu, total_q=rows + 1, total_k=rows + 1))
+    assert e.value.name == "ERR_UNSUPPORTED"
+
+
 def bwd_status(desc, q, k, v, o, lse, do, dlse, dq, dk, dv, ws):
     return status_of(S.sdpa_bwd_validate, desc, q, k, v, o, lse, do, dlse, dq, dk, dv, ws)
 
