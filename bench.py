@@ -52,10 +52,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# headers every kernel source includes (device helpers, parameter blocks, tile sizes)
+KERNEL_HEADERS = ("device.h", "params.h", "tiles.h", "launch.h", "profile.h")
+
+
 def source_hash(kernel: str) -> str:
     files = KERNEL_SOURCES[kernel]
     h = hashlib.sha256()
-    for name in (files,) if isinstance(files, str) else files:
+    for name in ((files,) if isinstance(files, str) else files) + KERNEL_HEADERS:
         with open(os.path.join(ROOT, "scaled_dot_product_05_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -157,10 +157,13 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
 // dst + 16 * i (dst wave-uniform), read from the resource at byte offset voff.  Issued as
 // inline assembly so that the compiler does not order later LDS reads behind it (it
 // cannot tell which LDS bytes the load writes); the caller waits with vm_wait and a
-// barrier before the destination is read.
+// barrier before the destination is read.  The load reads its LDS address from M0, which
+// the compiler writes with a scalar instruction just before; that write needs one wait
+// state before an LDS DMA reads it (the compiler pads its own LDS DMA the same way, but
+// does not look inside inline assembly), hence the s_nop.
 __device__ __forceinline__ void dma16(i32x4_t r, lds_t* dst, uint32_t voff) {
   const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
-  asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds" : : "{m0}"(d), "v"(voff), "s"(r) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "{m0}"(d), "v"(voff), "s"(r) : "memory");
 }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -169,10 +172,10 @@ __device__ __forceinline__ uint4 lds_read16(const lds_t* p) {
 }
 
 // 4 bytes per lane straight into LDS: lane i lands at dst + 4 * i (dst wave-uniform);
-// lanes outside the exec mask load nothing.
+// lanes outside the exec mask load nothing.  The same wait state after the M0 write.
 __device__ __forceinline__ void dma4(i32x4_t r, lds_t* dst, uint32_t voff) {
   const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
-  asm volatile("buffer_load_dword %1, %2, 0 offen lds" : : "{m0}"(d), "v"(voff), "s"(r) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" : : "{m0}"(d), "v"(voff), "s"(r) : "memory");
 }
 
 // ds_read_b64_tr_b16: lane 16g + 4a + b receives element b of the 8-byte rows addressed by
