@@ -10,9 +10,9 @@ them: the graph reads the live buffers, not values of the capture.
 Covered: the THD scheduler and the two-launch backward (C4), the split key tiles with their
 combine launch (C4 with one dominant sequence), the small-grid GQA halves with their
 arrival counters (zeroed by the pre-pass kernel on every call), a window with dLSE, fp32,
-the backward that allocates nothing (its static scratch buffer), the LSE merge, the
-block-mask build with the masked forward and backward, and the context-parallel ring
-emulation."""
+the backward that allocates nothing (its static scratch buffer), the FP8 forward, the LSE
+merge, the block-mask build with the masked forward and backward, and the
+context-parallel ring emulation."""
 import numpy as np
 import pytest
 import torch
@@ -57,7 +57,11 @@ def _replays_match_eager(run, inputs, outputs, name):
             assert torch.equal(_bits(t), e), f"{name}: replay {r}, output {i} differs from eager"
     gen = torch.Generator(device=DEV).manual_seed(7)
     for t in inputs:
-        t.copy_(torch.randn(t.shape, generator=gen, device=DEV, dtype=torch.float32).to(t.dtype))
+        if t.dtype == torch.uint8:  # E4M3 codes: finite ones only (0x7f / 0xff are NaN)
+            t.copy_(torch.randint(0, 0x7f, t.shape, generator=gen, device=DEV, dtype=torch.int32).to(t.dtype) |
+                    (torch.randint(0, 2, t.shape, generator=gen, device=DEV, dtype=torch.int32) << 7).to(t.dtype))
+        else:
+            t.copy_(torch.randn(t.shape, generator=gen, device=DEV, dtype=torch.float32).to(t.dtype))
     run()
     torch.cuda.synchronize()
     ref = [_bits(t).clone() for t in outputs]
@@ -119,6 +123,21 @@ def test_graph_replays_attention(name):
                         with_grad=True, name="graph_f32")
     run, inputs, outputs, _ = _attention_case(w, dlse, noalloc=name.startswith("noalloc"))
     _replays_match_eager(run, inputs, outputs, name)
+
+
+def test_graph_replays_fp8_forward():
+    say("case graph fp8 forward")
+    b, s, hq, hk, d = 2, 640, 4, 2, 128
+    coded = [synth.e4m3_codes(synth.normal(10, 45, i, (b, s, h, d))) for i, h in enumerate((hq, hk, hk))]
+    q, k, v = (c.to(DEV) for c, _ in coded)
+    ds = [torch.tensor([x], dtype=torch.float32, device=DEV) for _, x in coded]
+    o = torch.empty((b, s, hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((b, hq, s), dtype=torch.float32, device=DEV)
+
+    def run():
+        S.forward_fp8(q, k, v, "bshd", d ** -0.5, *ds, window=(-1, 0), out=o, lse=lse)
+
+    _replays_match_eager(run, [q, k, v], [o, lse], "fp8 forward")
 
 
 def test_graph_replays_merge():
