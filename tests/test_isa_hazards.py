@@ -1,10 +1,14 @@
-"""The HBM-to-LDS loads are inline assembly, so the compiler's hazard checks do not see them.
+"""Checks on the gfx950 assembly of the kernel sources, compiled with the library's own flags
+(host-only: hipcc cross-compiles; about a minute).
+
+The HBM-to-LDS loads are inline assembly, so the compiler's hazard checks do not see them.
 A `buffer_load ... lds` takes its LDS address from M0, and the compiler writes M0 with a
 scalar instruction just before each one; on gfx950 an LDS DMA must not read M0 in the
-cycle after that write (the compiler pads its own LDS DMA with an `s_nop 0` there).  This
-compiles the kernel sources to gfx950 assembly with the library's own flags and checks
-that every LDS DMA has at least one instruction after the last write of M0 before it.
-Host-only (hipcc cross-compiles); about a minute."""
+cycle after that write (the compiler pads its own LDS DMA with an `s_nop 0` there).  Every
+LDS DMA must have at least one instruction after the last write of M0 before it.
+
+No kernel may spill to scratch memory, except the block-mask head_dim-64 forward, whose
+three-workgroups-per-CU register budget leaves three values (16 bytes) on the stack."""
 import os
 import re
 import subprocess
@@ -49,12 +53,37 @@ def _m0_gaps(path):
     return gaps
 
 
-def test_lds_dma_waits_one_state_after_m0(tmp_path):
+def _scratch(path):
+    """{kernel symbol: private segment bytes} of every kernel in the assembly."""
+    txt = open(path).read()
+    out = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", txt, re.S):
+        out[m.group(1)] = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2)).group(1))
+    return out
+
+
+@pytest.fixture(scope="module")
+def assembly(tmp_path_factory):
     if not os.path.exists(B.HIPCC):
         pytest.skip("hipcc not available")
+    d = str(tmp_path_factory.mktemp("isa"))
     with ThreadPoolExecutor(max_workers=len(DMA_SOURCES)) as ex:
-        paths = list(ex.map(lambda s: _assembly(s, str(tmp_path)), DMA_SOURCES))
-    for src, path in zip(DMA_SOURCES, paths):
+        return dict(zip(DMA_SOURCES, ex.map(lambda s: _assembly(s, d), DMA_SOURCES)))
+
+
+def test_lds_dma_waits_one_state_after_m0(assembly):
+    for src, path in assembly.items():
         gaps = _m0_gaps(path)
         assert gaps, f"{src}: no LDS DMA found"
         assert min(gaps) >= 1, f"{src}: {gaps.count(0)} LDS DMAs read M0 right after its write"
+
+
+def test_no_kernel_spills(assembly):
+    # the block-mask D64 forward: fwd16p_kernel<BF, 64, ..., BSM = true>
+    allowed = re.compile(r"fwd16p_kernelILb[01]ELi64E.*ELb1EEEv")
+    for src, path in assembly.items():
+        sizes = _scratch(path)
+        assert sizes, f"{src}: no kernels found"
+        for name, n in sizes.items():
+            limit = 16 if allowed.search(name) else 0
+            assert n <= limit, f"{src}: {name} uses {n} bytes of scratch"
