@@ -116,7 +116,11 @@ typedef struct sdpa_rowstat {
  *             used).  Entries are clamped to [0, total] on the device.
  * block_mask  optional (NULL: none): a block-sparse element mask, see sdpa_block_mask_t.
  *             Key j is then visible to query i iff the window admits it AND the mask bit
- *             (i, j) is set.  BSHD, SBHD and BHSD only. */
+ *             (i, j) is set.  BSHD, SBHD and BHSD only.
+ * Size limit (ERR_UNSUPPORTED, before any launch): query rows times heads_q plus key rows
+ * times heads_kv, rows padded to multiples of 128 per sequence (THD: total plus 128 per
+ * sequence), must stay below 2^30, since a kernel launch counts its work-items in 32 bits
+ * (with 64 heads, 2^23 query and key rows each are refused). */
 /* Block-sparse mask (FlexAttention's BlockMask model: "Significant Accuracy Difference
  * between Compiled and Eager Flex Attention", PyTorch issue 135161, builds its masks with
  * create_block_mask from predicates over (q_idx, kv_idx) and passes them as block_mask=).
